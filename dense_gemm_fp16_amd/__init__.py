@@ -1,0 +1,183 @@
+"""Python binding of the MI355X fp16 TN GEMM library (libgemm_tn.so).
+
+Argument marshalling only: every step of the GEMM runs in the HIP kernels
+behind the C ABI declared in include/gemm_tn.h.  Torch supplies device
+memory and the current HIP stream.  There is no fallback: if the compiled
+library is missing, importing the package raises ImportError.
+
+    D = gemm_tn(A, B, alpha=1.0, beta=0.0, C=None, out_dtype=torch.float16)
+
+A: (M, K) or (batch, M, K) float16, B: (N, K) or (batch, N, K) float16,
+both contiguous on the GPU; C / D: (M, N) or (batch, M, N) of out_dtype.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgemm_tn.so")
+
+GEMM_TN_F16, GEMM_TN_F32 = 0, 1
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(5)
+
+# torch bundles its own HIP runtime under the same soname as the system one
+# (libamdhip64.so.7).  Whichever is loaded first serves the whole process, so
+# torch is imported before the library: its streams and allocations and our
+# launches then go through one runtime.
+import torch  # noqa: E402,F401
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is not built; run `python -m dense_gemm_fp16_amd.build` "
+        "(or __graft_entry__.build()) first")
+
+_lib = ctypes.CDLL(LIB_PATH)
+_i64, _f32, _vp, _int = (ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                         ctypes.c_int)
+_lib.gemm_tn.restype = _int
+_lib.gemm_tn.argtypes = [_i64, _i64, _i64, _f32, _vp, _vp, _f32, _vp, _vp,
+                         _int, _vp]
+_lib.gemm_tn_strided_batched.restype = _int
+_lib.gemm_tn_strided_batched.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp,
+                                         _i64, _vp, _i64, _f32, _vp, _i64,
+                                         _vp, _i64, _int, _vp]
+_lib.gemm_tn_describe.restype = _int
+_lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _i64, _f32, _int, _int, ctypes.c_char_p,
+                                  _i64]
+_lib.gemm_tn_status_string.restype = ctypes.c_char_p
+_lib.gemm_tn_status_string.argtypes = [_int]
+_lib.gemm_tn_version.restype = _int
+_lib.gemm_tn_version.argtypes = []
+
+EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_describe",
+           "gemm_tn_status_string", "gemm_tn_version")
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"gemm_tn failed: {status_string(status)} "
+                         f"(status {status})")
+
+
+def status_string(status: int) -> str:
+    return _lib.gemm_tn_status_string(status).decode()
+
+
+def version() -> tuple[int, int]:
+    v = _lib.gemm_tn_version()
+    return v >> 16, v & 0xFFFF
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library (for callers that pass raw pointers)."""
+    return _lib
+
+
+def describe(batch, M, N, K, beta=0.0, out_dtype="f16", aligned16=True,
+             strides=None) -> str:
+    """Kernel configuration the library picks for this problem."""
+    if strides is None:
+        strides = (M * K, N * K, M * N, M * N)
+    buf = ctypes.create_string_buffer(256)
+    _lib.gemm_tn_describe(batch, M, N, K, *strides, float(beta),
+                          GEMM_TN_F16 if out_dtype == "f16" else GEMM_TN_F32,
+                          1 if aligned16 else 0, buf, len(buf))
+    return buf.value.decode()
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(dt) -> int:
+    torch = _torch()
+    if dt == torch.float16:
+        return GEMM_TN_F16
+    if dt == torch.float32:
+        return GEMM_TN_F32
+    raise TypeError("C / D must be float16 or float32")
+
+
+def _stream_handle(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _check_operand(t, name):
+    torch = _torch()
+    if t.dtype != torch.float16:
+        raise TypeError(f"{name} must be float16")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major)")
+
+
+def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
+            out_dtype=None, stream=None):
+    """D = alpha * A @ B^T + beta * C on the GPU (2-D or batched 3-D).
+
+    `out` may be given (it is then D and is returned); otherwise D is
+    allocated with `out_dtype` (default: C's dtype, else float16)."""
+    torch = _torch()
+    _check_operand(A, "A")
+    _check_operand(B, "B")
+    if A.dim() != B.dim() or A.dim() not in (2, 3):
+        raise ValueError("A and B must both be 2-D or both 3-D")
+    batched = A.dim() == 3
+    if batched:
+        batch, M, K = A.shape
+        if B.shape[0] != batch or B.shape[2] != K:
+            raise ValueError("B must be (batch, N, K)")
+        N = B.shape[1]
+        shape = (batch, M, N)
+    else:
+        M, K = A.shape
+        if B.shape[1] != K:
+            raise ValueError("B must be (N, K)")
+        N = B.shape[0]
+        batch, shape = 1, (M, N)
+    if out is None:
+        dt = out_dtype if out_dtype is not None else (
+            C.dtype if C is not None else torch.float16)
+        out = torch.empty(shape, dtype=dt, device=A.device)
+    if tuple(out.shape) != shape or not out.is_contiguous() or not out.is_cuda:
+        raise ValueError(f"out must be a contiguous GPU tensor of shape {shape}")
+    code = _dtype_code(out.dtype)
+    c_ptr = None
+    if beta != 0.0:
+        if C is None:
+            raise ValueError("beta != 0 needs C")
+        if (tuple(C.shape) != shape or C.dtype != out.dtype
+                or not C.is_contiguous() or not C.is_cuda):
+            raise ValueError("C must match D's shape and dtype, contiguous")
+        c_ptr = C.data_ptr()
+    st = _lib.gemm_tn_strided_batched(
+        batch, M, N, K, float(alpha), A.data_ptr(), M * K, B.data_ptr(),
+        N * K, float(beta), c_ptr, M * N, out.data_ptr(), M * N, code,
+        _stream_handle(stream))
+    if st != OK:
+        raise GemmError(st)
+    return out
+
+
+def gemm_tn_strided_batched(batch, M, N, K, alpha, A_ptr, strideA, B_ptr,
+                            strideB, beta, C_ptr, strideC, D_ptr, strideD,
+                            d_dtype, stream_handle) -> int:
+    """Raw-pointer call of the C entry point; returns the status code."""
+    return _lib.gemm_tn_strided_batched(batch, M, N, K, float(alpha), A_ptr,
+                                        strideA, B_ptr, strideB, float(beta),
+                                        C_ptr, strideC, D_ptr, strideD,
+                                        d_dtype, stream_handle)
+
+
+def gemm_tn_raw(M, N, K, alpha, A_ptr, B_ptr, beta, C_ptr, D_ptr, d_dtype,
+                stream_handle) -> int:
+    """Raw-pointer call of gemm_tn(); returns the status code."""
+    return _lib.gemm_tn(M, N, K, float(alpha), A_ptr, B_ptr, float(beta),
+                        C_ptr, D_ptr, d_dtype, stream_handle)

@@ -1,0 +1,209 @@
+// extern "C" entry points of the fp16 TN GEMM library (declared in
+// include/gemm_tn.h): argument checks, configuration choice, the split-K
+// workspace, and the launches.
+#include <hip/hip_runtime.h>
+
+#include <map>
+#include <mutex>
+#include <utility>
+
+#include "gemm_tn.h"
+#include "gemm_tn_launch.hpp"
+#include "gemm_tn_plan.hpp"
+
+namespace gtn {
+
+hipError_t launch_splitk_reduce(const GemmArgs &a, bool out_f32, bool vec_out,
+                                hipStream_t s)
+{
+    const int64_t work = (int64_t)a.batch * a.M * ((a.N + 3) / 4);
+    const unsigned grid = (unsigned)((work + 255) / 256);
+    void *fn;
+    if (out_f32)
+        fn = vec_out ? (void *)&splitk_reduce_kernel<float, true>
+                     : (void *)&splitk_reduce_kernel<float, false>;
+    else
+        fn = vec_out ? (void *)&splitk_reduce_kernel<_Float16, true>
+                     : (void *)&splitk_reduce_kernel<_Float16, false>;
+    GemmArgs copy = a;
+    void *args[] = {&copy};
+    return hipLaunchKernel(fn, dim3(grid), dim3(256), args, 0, s);
+}
+
+namespace {
+
+// Split-K workspace, one per (device, stream): calls on one stream run in
+// order, so reusing its buffer is safe; distinct streams never share one.
+struct Workspace {
+    void *ptr = nullptr;
+    int64_t bytes = 0;
+};
+std::mutex g_ws_lock;
+std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
+
+int get_workspace(hipStream_t s, int64_t bytes, float **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess)
+        return GEMM_TN_ERR_LAUNCH;
+    std::lock_guard<std::mutex> g(g_ws_lock);
+    Workspace &w = g_ws[std::make_pair(dev, s)];
+    if (w.bytes < bytes) {
+        if (w.ptr) {
+            // earlier work on this stream may still read the old buffer
+            if (hipStreamSynchronize(s) != hipSuccess)
+                return GEMM_TN_ERR_WORKSPACE;
+            (void)hipFree(w.ptr);
+            w.ptr = nullptr;
+            w.bytes = 0;
+        }
+        int64_t want = bytes + bytes / 4;   // headroom for growth
+        if (hipMalloc(&w.ptr, (size_t)want) != hipSuccess) {
+            w.ptr = nullptr;
+            (void)hipGetLastError();
+            return GEMM_TN_ERR_WORKSPACE;
+        }
+        w.bytes = want;
+    }
+    *out = (float *)w.ptr;
+    return GEMM_TN_OK;
+}
+
+bool aligned(const void *p, uintptr_t a)
+{
+    return ((uintptr_t)p % a) == 0;
+}
+
+int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
+        const void *A, int64_t sA, const void *B, int64_t sB, float beta,
+        const void *C, int64_t sC, void *D, int64_t sD, int d_dtype,
+        void *stream)
+{
+    int st = check_sizes(batch, M, N, K, sA, sB, sC, sD, d_dtype);
+    if (st != GEMM_TN_OK)
+        return st;
+    if (batch == 0 || M == 0 || N == 0)
+        return GEMM_TN_OK;
+    st = check_pointers(M, N, K, A, B, beta, C, D);
+    if (st != GEMM_TN_OK)
+        return st;
+
+    const bool out_f32 = d_dtype == GEMM_TN_F32;
+    const int es = out_f32 ? 4 : 2;
+    const bool vec_in = aligned(A, 16) && aligned(B, 16) && K % 8 == 0 &&
+                        sA % 8 == 0 && sB % 8 == 0;
+    const bool vec_out = aligned(D, 4 * es) && N % 4 == 0 && sD % 4 == 0 &&
+                         (beta == 0.0f || (aligned(C, 4 * es) && sC % 4 == 0));
+    const Plan p = make_plan(batch, M, N, K, sA, sB, sC, sD, d_dtype, vec_in,
+                             vec_out, getenv("GEMM_TN_FORCE"));
+    if (p.status != GEMM_TN_OK)
+        return p.status;
+
+    hipStream_t s = (hipStream_t)stream;
+    GemmArgs a;
+    a.A = (const _Float16 *)A;
+    a.B = (const _Float16 *)B;
+    a.C = C;
+    a.D = D;
+    a.ws = nullptr;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.sA = sA;
+    a.sB = sB;
+    a.sC = sC;
+    a.sD = sD;
+    a.ws_ld = p.ws_ld;
+    a.alpha = alpha;
+    a.beta = beta;
+    a.tiles_m = p.tiles_m;
+    a.tiles_n = p.tiles_n;
+    a.batch = (int)batch;
+    a.splits = p.splits;
+    a.k_split = (int)p.k_split;
+    a.group_m = p.group_m;
+    const bool split = p.splits > 1;
+    if (split) {
+        st = get_workspace(s, p.ws_bytes, &a.ws);
+        if (st != GEMM_TN_OK)
+            return st;
+    }
+    hipError_t e;
+    switch (p.tile) {
+    case TILE_256:
+        e = launch_tile256(a, p.loader, out_f32, split, p.vec_out,
+                           (unsigned)p.grid, s);
+        break;
+    case TILE_128:
+        e = launch_tile128(a, p.loader, out_f32, split, p.vec_out,
+                           (unsigned)p.grid, s);
+        break;
+    default:
+        e = launch_tile64(a, p.loader, out_f32, split, p.vec_out,
+                          (unsigned)p.grid, s);
+        break;
+    }
+    if (e == hipSuccess && split)
+        e = launch_splitk_reduce(a, out_f32, p.vec_out, s);
+    return e == hipSuccess ? GEMM_TN_OK : GEMM_TN_ERR_LAUNCH;
+}
+
+}  // namespace
+}  // namespace gtn
+
+extern "C" {
+
+int gemm_tn(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+            const void *B, float beta, const void *C, void *D, int d_dtype,
+            void *stream)
+{
+    return gtn::run(1, M, N, K, alpha, A, 0, B, 0, beta, C, 0, D, 0, d_dtype,
+                    stream);
+}
+
+int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                            float alpha, const void *A, int64_t strideA,
+                            const void *B, int64_t strideB, float beta,
+                            const void *C, int64_t strideC, void *D,
+                            int64_t strideD, int d_dtype, void *stream)
+{
+    return gtn::run(batch, M, N, K, alpha, A, strideA, B, strideB, beta, C,
+                    strideC, D, strideD, d_dtype, stream);
+}
+
+int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     int64_t strideA, int64_t strideB, int64_t strideC,
+                     int64_t strideD, float beta, int d_dtype, int aligned16,
+                     char *buf, int64_t buflen)
+{
+    const bool vec_in = aligned16 && K % 8 == 0 && strideA % 8 == 0 &&
+                        strideB % 8 == 0;
+    const bool vec_out = aligned16 && N % 4 == 0 && strideD % 4 == 0 &&
+                         (beta == 0.0f || strideC % 4 == 0);
+    const gtn::Plan p = gtn::make_plan(batch, M, N, K, strideA, strideB,
+                                       strideC, strideD, d_dtype, vec_in,
+                                       vec_out, getenv("GEMM_TN_FORCE"));
+    return gtn::describe_plan(p, buf, buflen);
+}
+
+const char *gemm_tn_status_string(int status)
+{
+    switch (status) {
+    case GEMM_TN_OK:
+        return "ok";
+    case GEMM_TN_ERR_INVALID_ARG:
+        return "invalid argument";
+    case GEMM_TN_ERR_UNSUPPORTED:
+        return "unsupported size";
+    case GEMM_TN_ERR_LAUNCH:
+        return "kernel launch failed";
+    case GEMM_TN_ERR_WORKSPACE:
+        return "split-K workspace allocation failed";
+    default:
+        return "unknown status";
+    }
+}
+
+int gemm_tn_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+// Host-side argument checking and kernel-configuration choice for the fp16
+// TN GEMM.  Pure C++: no HIP call is made here, so every error path can be
+// exercised on a machine without a GPU.
+#pragma once
+
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "gemm_tn.h"
+
+namespace gtn {
+
+// Loader kinds (must match the kernel template's Loader enum).
+enum { PLAN_LOAD_DIRECT = 0, PLAN_LOAD_VREG = 1, PLAN_LOAD_ELEM = 2 };
+// Tile shapes, all with BK = 64 and 2 x 2 waves.
+enum { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, NUM_TILES = 3 };
+
+constexpr int kTileDim[NUM_TILES] = {256, 128, 64};
+constexpr int kBK = 64;
+constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
+
+// Addressing limits: the kernels form 32-bit byte offsets relative to the
+// first row of a tile (at most 256 rows), so a row may hold at most 2^21
+// fp16 operand elements (K) or 2^20 output elements (N, fp32).
+constexpr int64_t kMaxK = int64_t(1) << 21;
+constexpr int64_t kMaxN = int64_t(1) << 20;
+constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
+
+// Vector loader used when alignment allows it.
+constexpr int kDefaultVecLoader = PLAN_LOAD_VREG;
+
+struct Plan {
+    int status = GEMM_TN_OK;
+    bool noop = false;       // nothing to compute (batch, M or N is 0)
+    int tile = TILE_64;
+    int bm = 64, bn = 64;
+    int loader = PLAN_LOAD_ELEM;
+    bool vec_out = false;
+    int splits = 1;
+    int64_t k_split = 0;
+    int group_m = 8;
+    int tiles_m = 0, tiles_n = 0;
+    int64_t grid = 0;
+    int64_t ws_ld = 0;
+    int64_t ws_bytes = 0;
+};
+
+inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+inline bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    return !__builtin_mul_overflow(a, b, out);
+}
+
+// Size, stride and dtype checks (no pointers involved).
+inline int check_sizes(int64_t batch, int64_t M, int64_t N, int64_t K,
+                       int64_t sA, int64_t sB, int64_t sC, int64_t sD,
+                       int d_dtype)
+{
+    if (batch < 0 || M < 0 || N < 0 || K < 0)
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (d_dtype != GEMM_TN_F16 && d_dtype != GEMM_TN_F32)
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (sA < 0 || sB < 0 || sC < 0 || sD < 0)
+        return GEMM_TN_ERR_INVALID_ARG;
+    int64_t mk, nk, mn, t;
+    if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn))
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (!mul_ok(mn, 4, &t) || !mul_ok(mk, 2, &t) || !mul_ok(nk, 2, &t))
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (batch > 1) {
+        if (sD < mn)
+            return GEMM_TN_ERR_INVALID_ARG;  // batches of D would overlap
+        const int64_t strides[4] = {sA, sB, sC, sD};
+        for (int i = 0; i < 4; ++i) {
+            int64_t span;
+            if (!mul_ok(strides[i], batch - 1, &span) ||
+                !mul_ok(span + mn + mk + nk, 4, &t))
+                return GEMM_TN_ERR_INVALID_ARG;
+        }
+    }
+    if (batch == 0 || M == 0 || N == 0)
+        return GEMM_TN_OK;
+    if (K > kMaxK || N > kMaxN || M > kMaxM)
+        return GEMM_TN_ERR_UNSUPPORTED;
+    return GEMM_TN_OK;
+}
+
+inline int check_pointers(int64_t M, int64_t N, int64_t K, const void *A,
+                          const void *B, float beta, const void *C,
+                          const void *D)
+{
+    if (M == 0 || N == 0)
+        return GEMM_TN_OK;
+    if (D == nullptr)
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (K > 0 && (A == nullptr || B == nullptr))
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (beta != 0.0f && C == nullptr)
+        return GEMM_TN_ERR_INVALID_ARG;
+    return GEMM_TN_OK;
+}
+
+// Optional override for tuning sweeps: "tile=256|128|64,loader=0|1|2,
+// split=S,group=G" (any subset, comma separated).  Unknown keys are ignored;
+// a loader that the operands' alignment does not allow is ignored.
+struct Override {
+    int tile = -1, loader = -1, split = -1, group = -1;
+};
+
+inline Override parse_override(const char *s)
+{
+    Override o;
+    if (s == nullptr)
+        return o;
+    char buf[256];
+    strncpy(buf, s, sizeof buf - 1);
+    buf[sizeof buf - 1] = 0;
+    for (char *tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+        char *eq = strchr(tok, '=');
+        if (!eq)
+            continue;
+        *eq = 0;
+        const int v = atoi(eq + 1);
+        if (!strcmp(tok, "tile"))
+            o.tile = v == 256 ? TILE_256 : v == 128 ? TILE_128
+                   : v == 64  ? TILE_64  : -1;
+        else if (!strcmp(tok, "loader"))
+            o.loader = (v >= 0 && v <= 2) ? v : -1;
+        else if (!strcmp(tok, "split"))
+            o.split = v >= 1 ? v : -1;
+        else if (!strcmp(tok, "group"))
+            o.group = v >= 1 ? v : -1;
+    }
+    return o;
+}
+
+// Choose the kernel configuration.  vec_in: A and B 16-byte aligned, K and
+// the A/B batch strides multiples of 8.  vec_out: C (when read) and D
+// aligned to 4 elements, N and the C/D batch strides multiples of 4.
+inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
+                      int64_t sA, int64_t sB, int64_t sC, int64_t sD,
+                      int d_dtype, bool vec_in, bool vec_out,
+                      const char *override_spec)
+{
+    Plan p;
+    p.status = check_sizes(batch, M, N, K, sA, sB, sC, sD, d_dtype);
+    if (p.status != GEMM_TN_OK)
+        return p;
+    if (batch == 0 || M == 0 || N == 0) {
+        p.noop = true;
+        return p;
+    }
+    const Override o = parse_override(override_spec);
+
+    auto tiles = [&](int t) {
+        return cdiv(M, kTileDim[t]) * cdiv(N, kTileDim[t]) * batch;
+    };
+    // Largest tile that still gives every compute unit work.  The 256-wide
+    // tile needs one 128 KiB LDS double buffer per CU, so it is used only
+    // when there are about as many tiles as CUs and more than one k-tile.
+    int tile;
+    if (M >= 256 && N >= 256 && K > kBK && tiles(TILE_256) >= kCUs * 3 / 4)
+        tile = TILE_256;
+    else if (tiles(TILE_128) >= kCUs)
+        tile = TILE_128;
+    else
+        tile = TILE_64;
+    if (o.tile >= 0)
+        tile = o.tile;
+    p.tile = tile;
+    p.bm = p.bn = kTileDim[tile];
+    p.tiles_m = (int)cdiv(M, p.bm);
+    p.tiles_n = (int)cdiv(N, p.bn);
+    const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n * batch;
+
+    // Split K when the tiles alone leave CUs idle and K is long: aim for two
+    // workgroups per CU, with at least four k-tiles per slice.
+    int64_t splits = 1;
+    if (ntiles < kCUs && K >= 1024)
+        splits = cdiv(2 * kCUs, ntiles);
+    if (o.split >= 1)
+        splits = o.split;
+    const int64_t max_splits = K / (4 * kBK) > 1 ? K / (4 * kBK) : 1;
+    if (splits > max_splits)
+        splits = max_splits;
+    if (splits > 1) {
+        p.k_split = cdiv(cdiv(K, splits), kBK) * kBK;
+        splits = cdiv(K, p.k_split);
+    }
+    p.splits = (int)splits;
+    if (p.splits == 1)
+        p.k_split = cdiv(K, kBK) * kBK;
+
+    p.loader = vec_in ? kDefaultVecLoader : PLAN_LOAD_ELEM;
+    if (o.loader >= 0 && (vec_in || o.loader == PLAN_LOAD_ELEM))
+        p.loader = o.loader;
+    p.vec_out = vec_out;
+    p.group_m = tile == TILE_256 ? 4 : 8;
+    if (o.group >= 1)
+        p.group_m = o.group;
+
+    p.grid = ntiles * p.splits;
+    if (p.grid > 0x7FFFFFFF) {
+        p.status = GEMM_TN_ERR_UNSUPPORTED;
+        return p;
+    }
+    if (p.splits > 1) {
+        p.ws_ld = cdiv(N, 4) * 4;
+        p.ws_bytes = (int64_t)p.splits * batch * M * p.ws_ld * 4;
+    }
+    (void)d_dtype;
+    return p;
+}
+
+inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
+{
+    static const char *loaders[] = {"direct", "vreg", "elem"};
+    if (buf == nullptr || buflen <= 0)
+        return p.status;
+    if (p.status != GEMM_TN_OK) {
+        snprintf(buf, (size_t)buflen, "error:%d", p.status);
+        return p.status;
+    }
+    if (p.noop) {
+        snprintf(buf, (size_t)buflen, "noop");
+        return p.status;
+    }
+    snprintf(buf, (size_t)buflen,
+             "tile=%dx%dx%d waves=2x2 loader=%s split=%d k_split=%lld "
+             "vec_out=%d group_m=%d grid=%lld",
+             p.bm, p.bn, kBK, loaders[p.loader], p.splits,
+             (long long)p.k_split, p.vec_out ? 1 : 0, p.group_m,
+             (long long)p.grid);
+    return p.status;
+}
+
+}  // namespace gtn

@@ -1,0 +1,127 @@
+/*
+ * gemm_tn.h -- C ABI of the MI355X (gfx950) half-precision TN GEMM library.
+ *
+ *     D = alpha * A * B^T + beta * C
+ *
+ * The operation is the one the CuTe tutorial kernel gemm_device computes
+ * (page "gemm_device line-by-line walk-through", flagos.csdn.net, section 1:
+ * C = alpha*A*B + beta*C with B addressed as an N x K matrix), in the TN
+ * storage of page "cute(8) smem_gemm" (yuyanqi.com, kernel listing): A is
+ * M x K row-major, B is N x K row-major, so both operands are contiguous
+ * along K.  Readings where the pages are silent or disagree:
+ *   - accumulation is fp32 (the first page's kernel accumulates in fp16;
+ *     the fp32-accumulating atom of page "why retile_D", blog.qingsen.net,
+ *     section 2, is the one followed);
+ *   - C and D are separate arguments (C may equal D: every element of C is
+ *     read by the thread that writes the same element of D, before it
+ *     writes it);
+ *   - C is not read when beta == 0 (it may then be NULL; NaN in C does not
+ *     propagate); alpha is never special-cased;
+ *   - the fp32 result alpha*acc + beta*c is rounded to the output type with
+ *     round-to-nearest-even (fp16 overflow gives +-inf);
+ *   - K == 0 gives D = beta*C (an empty sum); M == 0 or N == 0 is a no-op.
+ *
+ * Layout: every matrix is packed row-major (lda = ldb = K, ldc = ldd = N).
+ * Element types: A and B are IEEE binary16; C and D share `d_dtype`.
+ *
+ * Ownership and asynchrony: the caller owns every buffer; they are device
+ * pointers (or any address the GPU can read/write, e.g. managed memory).
+ * The library never frees or retains them.  Calls enqueue work on `stream`
+ * (a hipStream_t, NULL for the default stream) and return at once; device
+ * faults surface at the caller's next synchronisation.  The only memory the
+ * library allocates itself is a per-(device, stream) fp32 workspace for the
+ * split-K path (skinny problems with a long K); it is grown on demand and
+ * kept until the process ends.
+ *
+ * Errors: every entry point returns a gemm_tn_status; the library never
+ * exits or aborts.  Arguments are fully validated before any HIP call, so
+ * an error return means nothing was enqueued.
+ *
+ * Thread safety: calls may come from several host threads.  Calls on
+ * different streams that both take the split-K path use different
+ * workspaces and do not race.
+ */
+#ifndef GEMM_TN_H
+#define GEMM_TN_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element type of C and D. */
+typedef enum gemm_tn_dtype {
+    GEMM_TN_F16 = 0, /* IEEE binary16 */
+    GEMM_TN_F32 = 1  /* IEEE binary32 */
+} gemm_tn_dtype;
+
+typedef enum gemm_tn_status {
+    GEMM_TN_OK = 0,
+    GEMM_TN_ERR_INVALID_ARG = 1, /* negative size, NULL where data is needed,
+                                    bad dtype, overlapping batch strides,
+                                    size overflow */
+    GEMM_TN_ERR_UNSUPPORTED = 2, /* sizes beyond the kernels' addressing
+                                    range: K > 2^22, N > 2^21 or
+                                    M > 2^31 - 1 */
+    GEMM_TN_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
+    GEMM_TN_ERR_WORKSPACE = 4    /* the split-K workspace could not be
+                                    allocated */
+} gemm_tn_status;
+
+/*
+ * One GEMM.  M, N, K >= 0.
+ *   A : M x K binary16, row-major (element (m,k) at A[m*K + k]); may be
+ *       NULL only when M*K == 0.
+ *   B : N x K binary16, row-major (element (n,k) at B[n*K + k]); may be
+ *       NULL only when N*K == 0.
+ *   C : M x N of d_dtype, row-major; read only when beta != 0 (then it must
+ *       not be NULL when M*N > 0); may equal D.
+ *   D : M x N of d_dtype, row-major; written (every element, nothing else).
+ *   d_dtype : GEMM_TN_F16 or GEMM_TN_F32.
+ *   stream  : hipStream_t to enqueue on.
+ * Any element-aligned pointer is accepted; 16-byte-aligned A/B with K a
+ * multiple of 8 select the vector loader, otherwise an element-granular
+ * loader runs (slower, same results).
+ */
+int gemm_tn(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
+            const void *B, float beta, const void *C, void *D, int d_dtype,
+            void *stream);
+
+/*
+ * `batch` independent GEMMs of the same shape, matrix i at
+ *   A + i*strideA,  B + i*strideB,  C + i*strideC,  D + i*strideD
+ * (strides in elements, >= 0; a zero A or B stride broadcasts one operand).
+ * Batches of D must not overlap: strideD >= M*N when batch > 1.  The
+ * batched score product S = Q * K^T of an attention head is this call with
+ * A = Q, B = K (page "why retile_D", blog.qingsen.net, section 1: Q is the
+ * A operand and K the B operand of the score GEMM).
+ */
+int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
+                            float alpha, const void *A, int64_t strideA,
+                            const void *B, int64_t strideB, float beta,
+                            const void *C, int64_t strideC, void *D,
+                            int64_t strideD, int d_dtype, void *stream);
+
+/*
+ * Name of the kernel configuration gemm_tn_strided_batched would launch for
+ * this problem (tile shape, loader, split-K factor), written NUL-terminated
+ * into buf (at most buflen bytes).  Pure host logic, no HIP call.  Returns
+ * GEMM_TN_OK or the status the GEMM call would return for these sizes.
+ */
+int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     int64_t strideA, int64_t strideB, int64_t strideC,
+                     int64_t strideD, float beta, int d_dtype,
+                     int aligned16, char *buf, int64_t buflen);
+
+/* Human-readable text of a status code (static storage). */
+const char *gemm_tn_status_string(int status);
+
+/* Library ABI version: (major << 16) | minor. */
+int gemm_tn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GEMM_TN_H */

@@ -1,0 +1,122 @@
+"""The C-ABI library on the CPU: it loads, exports what include/gemm_tn.h
+declares, rejects bad arguments before touching the GPU, and plans the
+expected kernel configurations.  No compute call is made here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_tn.h")
+
+g = pytest.importorskip("dense_gemm_fp16_amd")
+
+OK, INVALID, UNSUPPORTED = g.OK, g.ERR_INVALID_ARG, g.ERR_UNSUPPORTED
+F16, F32 = g.GEMM_TN_F16, g.GEMM_TN_F32
+# Dummy non-NULL addresses: argument checks never dereference them.
+P = ctypes.c_void_p(0x1000)
+NULL = None
+S = ctypes.c_void_p(0)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(gemm_tn\w*)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert names == sorted(g.EXPORTS)
+    lib = g.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_status_strings():
+    assert g.version() == (1, 0)
+    assert g.status_string(OK) == "ok"
+    assert g.status_string(INVALID) == "invalid argument"
+    assert g.status_string(99) == "unknown status"
+
+
+def call(M, N, K, A=P, B=P, beta=0.0, C=NULL, D=P, dt=F16, alpha=1.0):
+    return g.gemm_tn_raw(M, N, K, alpha, A, B, beta, C, D, dt, S)
+
+
+def batched(batch, M, N, K, sA, sB, sC, sD, beta=0.0, C=NULL, dt=F32):
+    return g.gemm_tn_strided_batched(batch, M, N, K, 1.0, P, sA, P, sB, beta,
+                                     C, sC, P, sD, dt, S)
+
+
+@pytest.mark.parametrize("args,status", [
+    (dict(M=-1, N=4, K=4), INVALID),
+    (dict(M=4, N=-1, K=4), INVALID),
+    (dict(M=4, N=4, K=-1), INVALID),
+    (dict(M=4, N=4, K=4, dt=2), INVALID),
+    (dict(M=4, N=4, K=4, dt=-1), INVALID),
+    (dict(M=4, N=4, K=4, D=NULL), INVALID),
+    (dict(M=4, N=4, K=4, A=NULL), INVALID),
+    (dict(M=4, N=4, K=4, B=NULL), INVALID),
+    (dict(M=4, N=4, K=4, beta=0.5, C=NULL), INVALID),
+    (dict(M=2 ** 40, N=2 ** 40, K=4), INVALID),         # M*N overflows bytes
+    (dict(M=4, N=4, K=2 ** 21 + 8), UNSUPPORTED),
+    (dict(M=4, N=2 ** 20 + 4, K=8), UNSUPPORTED),
+    (dict(M=2 ** 31, N=4, K=8), UNSUPPORTED),
+    # nothing to compute: OK without touching the GPU, NULLs allowed
+    (dict(M=0, N=4, K=4, A=NULL, B=NULL, D=NULL), OK),
+    (dict(M=4, N=0, K=4, A=NULL, B=NULL, D=NULL), OK),
+])
+def test_argument_checks(args, status):
+    assert call(**args) == status
+
+
+def test_batched_argument_checks():
+    # overlapping D batches
+    assert batched(2, 4, 4, 4, 16, 16, 16, 15) == INVALID
+    # negative strides
+    assert batched(2, 4, 4, 4, -16, 16, 16, 16) == INVALID
+    assert batched(-1, 4, 4, 4, 16, 16, 16, 16) == INVALID
+    # batch 0: no-op
+    assert batched(0, 4, 4, 4, 16, 16, 16, 16) == OK
+    # stride * batch overflow
+    assert batched(2 ** 40, 4, 4, 4, 2 ** 40, 16, 16, 16) == INVALID
+
+
+def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True):
+    d = g.describe(batch, M, N, K, beta, out, aligned)
+    return dict(kv.split("=") for kv in d.split()) if "=" in d else d
+
+
+def test_plans_for_the_workloads():
+    # 4096^3: one 256x256 tile per CU, vector loader, no split
+    p = describe(1, 4096, 4096, 4096)
+    assert p["tile"] == "256x256x64" and p["split"] == "1"
+    assert p["grid"] == "256" and p["loader"] != "elem"
+    # 1024^3 and the ragged 1000x1030x1000: 64x64 tiles, enough of them
+    assert describe(1, 1024, 1024, 1024, 0.5, "f32")["tile"] == "64x64x64"
+    p = describe(1, 1000, 1030, 1000, 0.0, "f32")
+    assert p["tile"] == "64x64x64" and p["vec_out"] == "0"   # N % 4 != 0
+    # skinny 128x4096x8192: split-K
+    p = describe(1, 128, 4096, 8192, 0.0, "f32")
+    assert int(p["split"]) > 1 and int(p["k_split"]) % 64 == 0
+    assert int(p["split"]) * int(p["k_split"]) >= 8192
+    # batched QK^T: 64 x (1024 x 1024 x 64)
+    p = describe(64, 1024, 1024, 64, 0.0, "f32")
+    assert p["tile"] == "128x128x64" and int(p["grid"]) == 64 * 64
+    # K not a multiple of 8, or misaligned: element loader
+    assert describe(1, 100, 100, 33)["loader"] == "elem"
+    assert describe(1, 128, 128, 64, aligned=False)["loader"] == "elem"
+    assert describe(1, 0, 5, 5) == "noop"
+
+
+def test_override_spec(monkeypatch):
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=128,split=2,loader=0,group=2")
+    p = describe(1, 512, 512, 1024)
+    assert p["tile"] == "128x128x64" and p["split"] == "2"
+    assert p["loader"] == "direct" and p["group_m"] == "2"
+    # a vector loader is refused when alignment does not allow it
+    p = describe(1, 512, 512, 1000 + 3)
+    assert p["loader"] == "elem"

@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Floating-point inputs must meet, element by element,
+    |d - ref| <= 1e-3*|ref| + 1e-4*sqrt(K)  (+ half an fp16 ulp if D is fp16)
+and integer-valued inputs in {-3..3} (exact in fp32 in any summation order)
+must match the correctly rounded oracle bit for bit.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import seeded_inputs as si
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import dense_gemm_fp16_amd as g
+    return g
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dt(out):
+    return torch.float16 if out == "f16" else torch.float32
+
+
+def run_gpu(w, out=None, **kw):
+    """Run workload w on the GPU; returns D as numpy (batch, M, N)."""
+    g = _gpu()
+    A = torch.from_numpy(np.ascontiguousarray(w.A)).cuda()
+    B = torch.from_numpy(np.ascontiguousarray(w.B)).cuda()
+    C = None
+    if w.C is not None:
+        C = torch.from_numpy(np.ascontiguousarray(w.C)).cuda()
+    D = g.gemm_tn(A, B, w.alpha, w.beta, C, out=out,
+                  out_dtype=_dt(w.out_dtype), **kw)
+    torch.cuda.synchronize()
+    return D.cpu().numpy()
+
+
+def sample_points(batch, M, N, n_random=4000, seed=0):
+    """Whole rows and columns at the edges and inside, plus random points."""
+    r = np.random.default_rng(seed)
+    pts = []
+    for b in sorted({0, batch - 1}):
+        for i in sorted({0, M // 2 + 1, M - 1}):
+            pts.append(np.stack([np.full(N, b), np.full(N, i), np.arange(N)], 1))
+        for j in sorted({0, N // 3, N - 1}):
+            pts.append(np.stack([np.full(M, b), np.arange(M), np.full(M, j)], 1))
+    pts.append(np.stack([r.integers(0, batch, n_random),
+                         r.integers(0, M, n_random),
+                         r.integers(0, N, n_random)], 1))
+    return np.concatenate(pts).astype(np.int64)
+
+
+FULL = ["c1_256", "c2_1024", "c4a_ragged", "c4b_skinny"]
+SAMPLED = ["c3_4096", "c5_qk"]
+
+
+@pytest.mark.parametrize("name", FULL + SAMPLED)
+def test_workload_tolerance(name):
+    w = si.workload(name)
+    _say(f"[parity] {name} {w.batch}x{w.M}x{w.N}x{w.K} out={w.out_dtype}")
+    d = run_gpu(w)
+    assert np.isfinite(d.astype(np.float64)).all()
+    if name in FULL:
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check(d, ref, w.K, w.out_dtype)
+    else:
+        pts = sample_points(w.batch, w.M, w.N)
+        ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
+        got = d[pts[:, 0], pts[:, 1], pts[:, 2]]
+        res = oracle.check(got, ref, w.K, w.out_dtype)
+    _say(f"[parity] {name}: {res}")
+    assert res.ok, str(res)
+
+
+@pytest.mark.parametrize("name", FULL + SAMPLED)
+def test_workload_integer_bit_exact(name):
+    w = si.workload(name, int_values=True)
+    _say(f"[exact] {name} {w.batch}x{w.M}x{w.N}x{w.K} out={w.out_dtype}")
+    d = run_gpu(w)
+    if name in FULL:
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(d, ref, w.out_dtype)
+    else:
+        pts = sample_points(w.batch, w.M, w.N, seed=1)
+        ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref,
+                                 w.out_dtype)
+    _say(f"[exact] {name}: {res}")
+    assert res.ok, str(res)
+
+
+def test_c5_full_batches():
+    # every element of a few whole batches of the attention-score product
+    w = si.workload("c5_qk")
+    d = run_gpu(w)
+    for b in (0, 17, 63):
+        ref = oracle.gemm_tn(w.A[b], w.B[b], w.alpha)
+        res = oracle.check(d[b], ref, w.K, w.out_dtype)
+        assert res.ok, f"batch {b}: {res}"
+
+
+EDGE = [1, 2, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 129, 255, 257]
+EDGE_SHAPES = sorted({(m, n, k) for m, n, k in [
+    *[(m, 64, 64) for m in EDGE], *[(64, n, 64) for n in EDGE],
+    *[(64, 64, k) for k in EDGE], (1, 1, 1), (257, 255, 129), (129, 257, 65),
+    (300, 260, 520), (513, 383, 200), (1, 777, 1024), (777, 1, 1024),
+    (96, 80, 1000), (2, 3, 4097)]})
+
+
+def _int_workload(batch, M, N, K, out, alpha=1.0, beta=0.0, seed=7):
+    return si.build(f"edge{M}x{N}x{K}", batch, M, N, K, alpha, beta, out,
+                    "int", seed + M * 7919 + N * 104729 + K, c_kind="int")
+
+
+@pytest.mark.parametrize("out", ["f16", "f32"])
+def test_edge_shapes_bit_exact(out):
+    for (M, N, K) in EDGE_SHAPES:
+        beta = 0.5 if (M + N) % 2 else 0.0
+        w = _int_workload(1, M, N, K, out, alpha=1.5, beta=beta)
+        _say(f"[edge] {M}x{N}x{K} out={out} beta={beta}")
+        d = run_gpu(w)
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(d, ref, out)
+        assert res.ok, f"{M}x{N}x{K} {out}: {res}"
+
+
+CONFIGS = [f"tile={t},loader={l},split={s}" for t in (256, 128, 64)
+           for l in (0, 1, 2) for s in (1, 3)]
+
+
+@pytest.mark.parametrize("spec", CONFIGS)
+def test_every_kernel_configuration(spec, monkeypatch):
+    """Each tile x loader x split-K instantiation on ragged shapes."""
+    monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    for (batch, M, N, K, out, beta) in [(1, 300, 260, 832, "f16", 0.0),
+                                        (2, 129, 200, 1000, "f32", -2.0),
+                                        (1, 512, 516, 768, "f32", 0.5)]:
+        w = _int_workload(batch, M, N, K, out, alpha=0.5, beta=beta)
+        _say(f"[config] {spec} {batch}x{M}x{N}x{K} {out}")
+        d = run_gpu(w)
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(d, ref, out)
+        assert res.ok, f"{spec} {M}x{N}x{K}: {res}"
+
+
+def test_unaligned_operands_and_odd_k():
+    g = _gpu()
+    r = np.random.default_rng(3)
+    M, N, K = 70, 90, 37
+    A = r.integers(-3, 4, (M * K + 1)).astype(np.float16)
+    B = r.integers(-3, 4, (N * K + 1)).astype(np.float16)
+    At = torch.from_numpy(A).cuda()[1:].view(M, K)   # 2-byte aligned
+    Bt = torch.from_numpy(B).cuda()[1:].view(N, K)
+    D = g.gemm_tn(At, Bt, out_dtype=torch.float32)
+    ref = oracle.gemm_tn(A[1:].reshape(M, K), B[1:].reshape(N, K))
+    assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok
+    # K multiple of 8 but misaligned base pointers
+    K = 64
+    A = r.integers(-3, 4, (M * K + 8)).astype(np.float16)
+    B = r.integers(-3, 4, (N * K)).astype(np.float16)
+    At = torch.from_numpy(A).cuda()[4:4 + M * K].view(M, K)  # 8-byte aligned
+    Bt = torch.from_numpy(B).cuda().view(N, K)
+    Dbuf = torch.empty(M * N + 1, dtype=torch.float32, device="cuda")
+    D = Dbuf[1:].view(M, N)                                  # 4-byte aligned
+    g.gemm_tn(At, Bt, out=D)
+    ref = oracle.gemm_tn(A[4:4 + M * K].reshape(M, K), B.reshape(N, K))
+    assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok
+
+
+def test_k_zero_gives_beta_c():
+    g = _gpu()
+    A = torch.empty(33, 0, dtype=torch.float16, device="cuda")
+    B = torch.empty(17, 0, dtype=torch.float16, device="cuda")
+    C = torch.randn(33, 17, device="cuda")
+    D = g.gemm_tn(A, B, 2.0, -0.5, C)
+    assert torch.equal(D, -0.5 * C)
+
+
+def test_beta_zero_ignores_nan_c_and_overwrites_d():
+    g = _gpu()
+    w = _int_workload(1, 100, 120, 96, "f32")
+    A = torch.from_numpy(w.A[0]).cuda()
+    B = torch.from_numpy(w.B[0]).cuda()
+    C = torch.full((100, 120), float("nan"), device="cuda")
+    D = torch.full((100, 120), float("nan"), device="cuda")
+    g.gemm_tn(A, B, 1.0, 0.0, C, out=D)
+    d = D.cpu().numpy()
+    assert np.isfinite(d).all()
+    assert oracle.check_exact(d, oracle.gemm_tn(w.A[0], w.B[0]), "f32").ok
+
+
+@pytest.mark.parametrize("out", ["f16", "f32"])
+def test_c_may_alias_d(out):
+    g = _gpu()
+    w = _int_workload(1, 200, 136, 256, out, alpha=1.0, beta=-1.0)
+    A = torch.from_numpy(w.A[0]).cuda()
+    B = torch.from_numpy(w.B[0]).cuda()
+    CD = torch.from_numpy(w.C[0].copy()).cuda()
+    g.gemm_tn(A, B, 1.0, -1.0, CD, out=CD)
+    ref = oracle.gemm_tn(w.A[0], w.B[0], 1.0, -1.0, w.C[0])
+    assert oracle.check_exact(CD.cpu().numpy(), ref, out).ok
+
+
+@pytest.mark.parametrize("shape", [(1, 130, 70, 200), (3, 64, 65, 64),
+                                   (1, 128, 4096, 8192)])
+def test_guard_bands_untouched(shape):
+    """Nothing outside D is written (sentinels before and after it)."""
+    g = _gpu()
+    batch, M, N, K = shape
+    w = _int_workload(batch, M, N, K, "f32")
+    A = torch.from_numpy(w.A).cuda()
+    B = torch.from_numpy(w.B).cuda()
+    pad = 4096
+    buf = torch.full((pad + batch * M * N + pad,), 12345.0, device="cuda")
+    D = buf[pad:pad + batch * M * N].view(batch, M, N)
+    g.gemm_tn(A, B, out=D)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:pad] == 12345.0) and torch.all(buf[-pad:] == 12345.0)
+    ref = oracle.gemm_tn(w.A, w.B)
+    assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok
+
+
+@pytest.mark.parametrize("name", ["c4b_skinny", "c3_4096", "c5_qk"])
+def test_two_runs_are_bitwise_equal(name):
+    w = si.workload(name)
+    d1 = run_gpu(w)
+    d2 = run_gpu(w)
+    assert np.array_equal(d1.view(np.uint8), d2.view(np.uint8))
+
+
+def test_batched_broadcast_operand():
+    g = _gpu()
+    batch, M, N, K = 5, 40, 48, 72
+    w = _int_workload(batch, M, N, K, "f32")
+    A = torch.from_numpy(w.A).cuda()
+    B0 = torch.from_numpy(w.B[0]).cuda()
+    D = torch.empty(batch, M, N, device="cuda")
+    st = g.gemm_tn_strided_batched(
+        batch, M, N, K, 1.0, A.data_ptr(), M * K, B0.data_ptr(), 0, 0.0,
+        None, 0, D.data_ptr(), M * N, g.GEMM_TN_F32,
+        torch.cuda.current_stream().cuda_stream)
+    assert st == g.OK
+    ref = oracle.gemm_tn(w.A, np.broadcast_to(w.B[0], (batch, N, K)))
+    assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok
+
+
+def test_fp16_overflow_rounds_to_inf():
+    g = _gpu()
+    K = 64
+    A = torch.full((32, K), 40.0, dtype=torch.float16, device="cuda")
+    B = torch.full((32, K), 30.0, dtype=torch.float16, device="cuda")
+    D = g.gemm_tn(A, B, out_dtype=torch.float16)   # 76800 > 65504
+    assert torch.isinf(D).all() and (D > 0).all()

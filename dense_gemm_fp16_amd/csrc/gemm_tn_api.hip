@@ -92,8 +92,9 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     const int es = out_f32 ? 4 : 2;
     const bool vec_in = aligned(A, 16) && aligned(B, 16) && K % 8 == 0 &&
                         sA % 8 == 0 && sB % 8 == 0;
-    const bool vec_out = aligned(D, 4 * es) && N % 4 == 0 && sD % 4 == 0 &&
-                         (beta == 0.0f || (aligned(C, 4 * es) && sC % 4 == 0));
+    const bool vec_out = aligned(D, 16) && (N * es) % 16 == 0 &&
+                         (sD * es) % 16 == 0 &&
+                         (beta == 0.0f || (aligned(C, 16) && (sC * es) % 16 == 0));
     const Plan p = make_plan(batch, M, N, K, sA, sB, sC, sD, d_dtype, vec_in,
                              vec_out, getenv("GEMM_TN_FORCE"));
     if (p.status != GEMM_TN_OK)
@@ -178,8 +179,10 @@ int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
 {
     const bool vec_in = aligned16 && K % 8 == 0 && strideA % 8 == 0 &&
                         strideB % 8 == 0;
-    const bool vec_out = aligned16 && N % 4 == 0 && strideD % 4 == 0 &&
-                         (beta == 0.0f || strideC % 4 == 0);
+    const int es = d_dtype == GEMM_TN_F32 ? 4 : 2;
+    const bool vec_out = aligned16 && (N * es) % 16 == 0 &&
+                         (strideD * es) % 16 == 0 &&
+                         (beta == 0.0f || (strideC * es) % 16 == 0);
     const gtn::Plan p = gtn::make_plan(batch, M, N, K, strideA, strideB,
                                        strideC, strideD, d_dtype, vec_in,
                                        vec_out, getenv("GEMM_TN_FORCE"));

@@ -1,0 +1,35 @@
+// Tile configurations: the k-depth BK and the LDS ring depth of each tile
+// shape.  Shared by the host planner and the kernel instantiations; the
+// macros exist so that tuning builds can try other values.
+#pragma once
+
+#ifndef GTN_T256_BK
+#define GTN_T256_BK 64
+#endif
+#ifndef GTN_T256_STAGES
+#define GTN_T256_STAGES 2
+#endif
+#ifndef GTN_T256_WM
+#define GTN_T256_WM 2
+#endif
+#ifndef GTN_T256_WN
+#define GTN_T256_WN 4
+#endif
+#ifndef GTN_T256_MINW
+#define GTN_T256_MINW 2
+#endif
+#ifndef GTN_T256_SCHED
+#define GTN_T256_SCHED 2
+#endif
+#ifndef GTN_T128_BK
+#define GTN_T128_BK 64
+#endif
+#ifndef GTN_T128_STAGES
+#define GTN_T128_STAGES 2
+#endif
+#ifndef GTN_T64_BK
+#define GTN_T64_BK 64
+#endif
+#ifndef GTN_T64_STAGES
+#define GTN_T64_STAGES 3
+#endif

@@ -14,11 +14,12 @@
 //    turns into zeros: that is the edge predication (page "Mat Transpose
 //    CuTe 版代码学习", chuoer47.github.io, version 1: a per-element coordinate
 //    mask decides which accesses happen).
-//  * LDS layout: chunk c of row r is stored at chunk c ^ ((r >> SWZ) & 7)
-//    of that row: an XOR swizzle of 16-byte groups, which keeps each group
-//    contiguous for 128-bit reads while spreading one logical chunk of
-//    consecutive rows over distinct banks (page "cute(8) smem_gemm",
-//    section 3: Swizzle<B,M,S> XORs the row bits into the group index).
+//  * LDS layout: chunk c of row r is stored at chunk c ^ f(r) of that row:
+//    an XOR swizzle of 16-byte groups, which keeps each group contiguous
+//    for 128-bit reads while spreading one logical chunk of consecutive
+//    rows over distinct banks (page "cute(8) smem_gemm", section 3:
+//    Swizzle<B,M,S> XORs the row bits into the group index); f is chosen
+//    for gfx950's 64-bank LDS (see swizzle_chunk).
 //  * LDS -> registers: v_mfma_f32_32x32x16_f16 takes, in each lane, 8
 //    consecutive-k halves of one row of each operand; in TN storage that is
 //    one ds_read_b128 per operand per lane, with no shuffle.
@@ -27,9 +28,10 @@
 //    accumulator block is D^T: each lane then holds 4 consecutive n of one
 //    m per group of 4 registers, which the epilogue stores as one 8- or
 //    16-byte vector.
-//  * Pipeline: two LDS stages; the loads of k-tile t+1 are issued before
-//    the MFMAs of k-tile t, and one barrier per k-tile orders both the
-//    read-after-write on stage t and the write-after-read on stage t+1.
+//  * Pipeline: a ring of LDS stages; the loads of k-tile t + STAGES - 1
+//    are in flight while k-tile t is multiplied, and one barrier per k-tile
+//    orders both the read-after-write on the next stage and the
+//    write-after-read on the stage being refilled.
 //  * Epilogue: alpha * acc (+ beta * C when beta != 0) in fp32, rounded to
 //    fp16 or fp32 with round-to-nearest-even, stored through buffer stores
 //    whose out-of-range lanes are dropped.
@@ -118,10 +120,60 @@ __device__ inline TileCoord map_tile(const GemmArgs &p)
     return tc;
 }
 
-template <int SWZ>
+// LDS swizzle of a tile with BK-element (2*BK-byte) rows.  gfx950's LDS has
+// 64 banks of 4 bytes and serves a ds_read_b128 16 lanes (256 bytes) at a
+// time, so the 16 rows read together by one lane group must fill the 16
+// distinct 16-byte bank slots of a 256-byte line.  A 256-byte line holds
+// R = 128 / BK rows; XORing the chunk index with (row / R) mod CHUNKS makes
+// the R rows of a line and the CHUNKS lines of a 16-row group land in
+// distinct slots for every logical chunk.  (Measured on MI355X: zero
+// SQ_LDS_BANK_CONFLICT with this map, half of all LDS cycles in conflict
+// with row mod 8, the map a 32-bank LDS would want.)
+template <int BK>
 __device__ __host__ constexpr int swizzle_chunk(int row, int chunk)
 {
-    return chunk ^ ((row >> SWZ) & 7);
+    return chunk ^ ((row / (128 / BK)) % (BK / 8));
+}
+
+template <bool V>
+struct Bool {
+    static constexpr bool value = V;
+};
+template <int V>
+struct Int {
+    static constexpr int value = V;
+};
+
+// s_waitcnt with only the vector-memory counter (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
+template <int N>
+__device__ inline void wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) |
+                               (15 << 8));
+}
+// s_waitcnt with only the LDS/scalar counter (lgkmcnt in bits 11:8).
+template <int N>
+__device__ inline void wait_lgkmcnt()
+{
+    static_assert(N >= 0 && N < 16, "lgkmcnt range");
+    __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4) | (N << 8));
+}
+
+// Workgroup barrier with no implied memory wait.  __syncthreads() also
+// releases every outstanding memory operation, which for the loads that
+// write LDS directly means waiting for all of them, including prefetches
+// meant to stay in flight across the barrier.  Callers wait explicitly for
+// exactly what the barrier must order (lgkmcnt for LDS reads and writes,
+// vmcnt for the direct-to-LDS loads of the tile about to be read); the
+// empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ inline void block_sync()
+{
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
 }
 
 template <typename OutT>
@@ -190,35 +242,62 @@ __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 
 // ---------------------------------------------------------------------------
 // Main kernel.
-//   BM x BN x BK : workgroup tile; WM x WN waves; SWZ : swizzle row shift;
+//   BM x BN x BK : workgroup tile (BK = 32 or 64); WM x WN waves;
+//   STAGES : LDS ring depth of the direct loader (tile t + STAGES - 1 is in
+//            flight while tile t is multiplied);
 //   LOADER : LOAD_DIRECT (16-byte buffer loads straight into LDS),
 //            LOAD_VREG (16-byte loads into VGPRs, then ds_write_b128),
-//            LOAD_ELEM (2-byte loads, any K and any alignment);
+//            LOAD_ELEM (2-byte loads, any K and any alignment); the two
+//            register-staged loaders use a ring of two stages;
+//   SCHED : with the direct loader, 0 = every wave interleaves its loads
+//           with its MFMAs; 1 = ping-pong (8 waves, two per SIMD: in each
+//           phase one wave of a SIMD multiplies a whole k-tile from
+//           registers while the other issues loads and fragment reads);
+//           2 = ping-pong with the tile loads split between the two wave
+//           groups (A ring of three stages, B ring of two);
 //   OutT : _Float16 or float; SPLIT : write fp32 partials to the workspace;
-//   VEC_OUT : D / C rows allow 4-element vector access (N % 4 == 0 and the
-//             base pointers are aligned for it).
+//   VEC_OUT : rows of D (and C) start on 16-byte boundaries (N * element
+//             size a multiple of 16, D / C 16-byte aligned): the tile is
+//             written through LDS with 16-byte stores.
 // ---------------------------------------------------------------------------
-template <int BM, int BN, int BK, int WM, int WN, int SWZ, int LOADER,
-          typename OutT, bool SPLIT, bool VEC_OUT, int MIN_WAVES>
+template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADER,
+          typename OutT, bool SPLIT, bool VEC_OUT, int MIN_WAVES, int SCHED>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64,
                                                            WM * WN * 64),
                                amdgpu_waves_per_eu(MIN_WAVES, 8)))
 gemm_tn_kernel(GemmArgs p)
 {
-    constexpr int NT = WM * WN * 64;
+    constexpr int NW = WM * WN;
+    constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
     constexpr int MI = WTM / 32, NI = WTN / 32;
     constexpr int KSTEPS = BK / 16;
     constexpr int CHUNKS = BK / 8;            // 16-byte chunks per tile row
     constexpr int ROWS_PER_WAVE_LOAD = 64 / CHUNKS;
     constexpr int STAGE_HALVES = (BM + BN) * BK;
-    static_assert(BK == 64, "the swizzle and loaders assume 128-byte rows");
+    static_assert(BK == 32 || BK == 64, "tile rows of 64 or 128 bytes");
+    static_assert(STAGES >= 2, "at least double buffering");
     static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 blocks");
-    static_assert(BM % (ROWS_PER_WAVE_LOAD * WM * WN) == 0 &&
-                      BN % (ROWS_PER_WAVE_LOAD * WM * WN) == 0,
+    static_assert(BM % (ROWS_PER_WAVE_LOAD * NW) == 0 &&
+                      BN % (ROWS_PER_WAVE_LOAD * NW) == 0,
                   "every wave issues the same number of tile loads");
+    // SCHED 2 keeps three stages of A and two of B (one more tile of A in
+    // flight); the other schedules keep STAGES stages of A and B together.
+    constexpr bool SPLIT_RING = SCHED == 2 && LOADER == LOAD_DIRECT;
+    constexpr int A_STAGES = SPLIT_RING ? 3 : STAGES;
+    constexpr int LDS_HALVES = SPLIT_RING ? (3 * BM + 2 * BN) * BK
+                                          : STAGES * STAGE_HALVES;
+    static_assert(LDS_HALVES * 2 <= 160 * 1024, "LDS budget");
+    // Element offsets of the A and B tiles of a stage.
+    auto a_base = [](int st) {
+        return SPLIT_RING ? st * BM * BK : st * STAGE_HALVES;
+    };
+    auto b_base = [](int st) {
+        return SPLIT_RING ? A_STAGES * BM * BK + st * BN * BK
+                          : st * STAGE_HALVES + BM * BK;
+    };
 
-    __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * STAGE_HALVES];
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[LDS_HALVES];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -251,57 +330,76 @@ gemm_tn_kernel(GemmArgs p)
             acc[i][j] = f32x16{};
 
     // ---- global -> LDS ----------------------------------------------------
-    // LOAD_DIRECT: wave w fills 8-row groups w, w + WM*WN, ... of the A and
-    // B tiles; lane l writes physical chunk l % 8 of row l / 8 of the group,
-    // so it fetches the logical chunk that the swizzle puts there.
-    constexpr int A_GROUPS = BM / ROWS_PER_WAVE_LOAD / (WM * WN);
-    constexpr int B_GROUPS = BN / ROWS_PER_WAVE_LOAD / (WM * WN);
-    // LOAD_VREG / LOAD_ELEM: thread t owns slots t, t + NT, ... of the
-    // (BM + BN) x CHUNKS chunk grid (row-major), A rows first.
-    constexpr int SLOTS = (BM + BN) * CHUNKS / NT;
-    static_assert((BM + BN) * CHUNKS % NT == 0, "slots divide evenly");
-
-    auto issue_direct = [&](int stage, int64_t k0) {
-        GTN_LDS _Float16 *base =
-            (GTN_LDS _Float16 *)(lds) + stage * STAGE_HALVES;
-        const int rrow = lane / CHUNKS, pch = lane % CHUNKS;
+    // LOAD_DIRECT: one buffer_load_dwordx4 ... lds of a wave fills
+    // ROWS_PER_WAVE_LOAD whole tile rows (1 KiB, written contiguously from
+    // the wave's LDS base); lane l lands in physical chunk l % CHUNKS of row
+    // l / CHUNKS of that group, so it fetches the logical chunk the swizzle
+    // maps there.  Wave w fills row groups w, w + NW, ... of A, then of B.
+    constexpr bool PINGPONG = (SCHED == 1 || SCHED == 2) &&
+                              LOADER == LOAD_DIRECT;
+    static_assert(!PINGPONG || (NW == 8 && STAGES == 2),
+                  "ping-pong: two waves per SIMD, double-buffered LDS");
+    // Waves that issue the tile loads: all of them, or the first half in
+    // the ping-pong schedule.
+    constexpr int NLOAD = PINGPONG ? NW / 2 : NW;
+    constexpr int A_GROUPS = BM / ROWS_PER_WAVE_LOAD / NLOAD;
+    constexpr int B_GROUPS = BN / ROWS_PER_WAVE_LOAD / NLOAD;
+    static_assert(A_GROUPS * ROWS_PER_WAVE_LOAD * NLOAD == BM &&
+                      B_GROUPS * ROWS_PER_WAVE_LOAD * NLOAD == BN,
+                  "loading waves cover the tile");
+    constexpr int LOADS_PER_TILE = A_GROUPS + B_GROUPS;
+    const int rrow = lane / CHUNKS, pch = lane % CHUNKS;
+    // Tile starting at k0 into LDS stage `stage` (issued by loading wave
+    // lw); chunks at or past k_end (and every chunk once k0 >= k_end) read
+    // as zero without touching memory.  Offsets are relative to the tile's
+    // first row; rows past M / N fall beyond the record count and read as
+    // zero.
+    // Loads [x0, x1) of the tile's list (A row groups, then B row groups).
+    // The swizzle repeats every 16 rows and a wave's row groups are
+    // NLOAD * ROWS_PER_WAVE_LOAD rows apart, so every group of a wave shares
+    // one per-lane chunk and offset; only a wave-uniform row stride differs.
+    static_assert((NLOAD * ROWS_PER_WAVE_LOAD) % 16 == 0,
+                  "a wave's row groups share the swizzle phase");
+    auto issue_part = [&](int stage, int64_t k0, int lw, int x0, int x1) {
+        GTN_LDS _Float16 *ldsp = (GTN_LDS _Float16 *)(lds);
+        const int64_t rem64 = k_end - k0;
+        const int rem = rem64 < 0 ? 0 : (rem64 > BK ? BK : (int)rem64);
+        const uint32_t kb = (uint32_t)(k0 < K ? k0 : K) * 2;
+        const int row0 = lw * ROWS_PER_WAVE_LOAD + rrow;
+        const int kc = swizzle_chunk<BK>(row0, pch) * 8;
+        const uint32_t lane_off = (uint32_t)(row0 * K + kc) * 2 + kb;
+        const bool valid = kc < rem;
+        const uint32_t group_stride =
+            (uint32_t)(NLOAD * ROWS_PER_WAVE_LOAD * K) * 2;
 #pragma unroll
-        for (int g = 0; g < A_GROUPS; ++g) {
-            const int grp = wave + g * WM * WN;
-            const int row = grp * ROWS_PER_WAVE_LOAD + rrow;
-            const int lch = swizzle_chunk<SWZ>(row, pch);
-            const int64_t kk = k0 + lch * 8;
-            const uint32_t off = kk < k_end
-                                     ? (uint32_t)((row * K + kk) * 2)
-                                     : kOutOfRange;
+        for (int x = 0; x < LOADS_PER_TILE; ++x) {
+            if (x < x0 || x >= x1)
+                continue;
+            const bool isA = x < A_GROUPS;
+            const int g = isA ? x : x - A_GROUPS;
+            const uint32_t off =
+                valid ? lane_off + (uint32_t)g * group_stride : kOutOfRange;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rA, (GTN_LDS void *)(base + grp * ROWS_PER_WAVE_LOAD * BK), 16,
-                off, 0, 0, 0);
-        }
-#pragma unroll
-        for (int g = 0; g < B_GROUPS; ++g) {
-            const int grp = wave + g * WM * WN;
-            const int row = grp * ROWS_PER_WAVE_LOAD + rrow;
-            const int lch = swizzle_chunk<SWZ>(row, pch);
-            const int64_t kk = k0 + lch * 8;
-            const uint32_t off = kk < k_end
-                                     ? (uint32_t)((row * K + kk) * 2)
-                                     : kOutOfRange;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rB,
-                (GTN_LDS void *)(base + BM * BK +
-                                 grp * ROWS_PER_WAVE_LOAD * BK),
+                isA ? rA : rB,
+                (GTN_LDS void *)(ldsp + (isA ? a_base(stage) : b_base(stage)) +
+                                 (lw + g * NLOAD) * ROWS_PER_WAVE_LOAD * BK),
                 16, off, 0, 0, 0);
         }
     };
+    auto issue_direct = [&](int stage, int64_t k0, int lw) {
+        issue_part(stage, k0, lw, 0, LOADS_PER_TILE);
+    };
 
+    // LOAD_VREG / LOAD_ELEM: thread t owns chunk slots t, t + NT, ... of the
+    // (BM + BN) x CHUNKS grid (row-major, A rows first).  Slot block i
+    // covers rows [i*RB, (i+1)*RB); RB divides BM, so a block lies wholly in
+    // A or wholly in B and the operand is a compile-time choice per i.
+    constexpr int SLOTS = (BM + BN) * CHUNKS / NT;
+    constexpr int RB = NT / CHUNKS;
+    static_assert((BM + BN) * CHUNKS % NT == 0, "slots divide evenly");
+    static_assert(BM % RB == 0, "slot blocks do not straddle A and B");
     u32x4 stage_regs[LOADER == LOAD_DIRECT ? 1 : SLOTS];
 
-    // Slot block i covers tile rows [i*RB, (i+1)*RB) of the A-then-B row
-    // list; RB divides BM, so a block lies wholly in A or wholly in B and
-    // the operand choice is a compile-time constant per i.
-    constexpr int RB = NT / CHUNKS;
-    static_assert(BM % RB == 0, "slot blocks do not straddle A and B");
     auto fetch_regs = [&](int64_t k0) {
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
@@ -334,106 +432,359 @@ gemm_tn_kernel(GemmArgs p)
     };
 
     auto store_regs = [&](int stage) {
-        _Float16 *base = lds + stage * STAGE_HALVES;
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const bool isA = i * RB < BM;
             const int row = (isA ? i * RB : i * RB - BM) + tid / CHUNKS;
-            const int pch = swizzle_chunk<SWZ>(row, tid % CHUNKS);
-            *(u32x4 *)(base + (isA ? 0 : BM * BK) + row * BK + pch * 8) =
-                stage_regs[i];
+            const int pch = swizzle_chunk<BK>(row, tid % CHUNKS);
+            *(u32x4 *)(lds + (isA ? a_base(stage) : b_base(stage)) +
+                       row * BK + pch * 8) = stage_regs[i];
         }
     };
 
-    // ---- MFMA on one LDS stage -------------------------------------------
-    auto compute = [&](int stage) {
-        const _Float16 *sA = lds + stage * STAGE_HALVES;
-        const _Float16 *sB = sA + BM * BK;
-        const int frow = lane & 31;
-        const int fhalf = lane >> 5;
+    // ---- LDS -> registers, and the MFMAs of one 16-wide k-step ---------
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    // Fragments are read in the order the MFMAs below consume them (B0, A0,
+    // then B1.., then A1..), so the first MFMAs of a k-step depend only on
+    // the oldest reads of the previous one.
+    auto read_frags2 = [&](int sta, int stb, int ks, half8 (&af)[MI],
+                           half8 (&bf)[NI]) {
+        const _Float16 *sA = lds + a_base(sta);
+        const _Float16 *sB = lds + b_base(stb);
+        const int ch = ks * 2 + fhalf;
+        auto rd_a = [&](int i) {
+            const int row = wm * WTM + i * 32 + frow;
+            af[i] = *(const half8 *)(sA + row * BK +
+                                     swizzle_chunk<BK>(row, ch) * 8);
+        };
+        auto rd_b = [&](int j) {
+            const int row = wn * WTN + j * 32 + frow;
+            bf[j] = *(const half8 *)(sB + row * BK +
+                                     swizzle_chunk<BK>(row, ch) * 8);
+        };
+        rd_b(0);
+        rd_a(0);
 #pragma unroll
-        for (int ks = 0; ks < KSTEPS; ++ks) {
-            half8 af[MI], bf[NI];
-            const int ch = ks * 2 + fhalf;
+        for (int j = 1; j < NI; ++j)
+            rd_b(j);
 #pragma unroll
-            for (int i = 0; i < MI; ++i) {
-                const int row = wm * WTM + i * 32 + frow;
-                af[i] = *(const half8 *)(sA + row * BK +
-                                         swizzle_chunk<SWZ>(row, ch) * 8);
-            }
-#pragma unroll
-            for (int j = 0; j < NI; ++j) {
-                const int row = wn * WTN + j * 32 + frow;
-                bf[j] = *(const half8 *)(sB + row * BK +
-                                         swizzle_chunk<SWZ>(row, ch) * 8);
-            }
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-#pragma unroll
-                for (int j = 0; j < NI; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                        bf[j], af[i], acc[i][j], 0, 0, 0);
-        }
+        for (int i = 1; i < MI; ++i)
+            rd_a(i);
     };
+    auto read_frags = [&](int stage, int ks, half8 (&af)[MI], half8 (&bf)[NI]) {
+        read_frags2(stage, stage, ks, af, bf);
+    };
+    auto mma = [&](const half8 (&af)[MI], const half8 (&bf)[NI]) {
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                    bf[j], af[i], acc[i][j], 0, 0, 0);
+    };
+    // Instruction order inside one k-step (the compiler otherwise waits on
+    // each fragment right before its first MFMA): the next k-step's
+    // fragment reads and this k-step's share of tile loads go out one each
+    // after an MFMA, from the start of the k-step.
+    constexpr int FRAGS = MI + NI;
+    constexpr int MFMAS = MI * NI;
 
     // ---- main loop -------------------------------------------------------
-    if (ktiles > 0) {
-        if (LOADER == LOAD_DIRECT) {
-            issue_direct(0, k_begin);
+    if (PINGPONG) {
+        // Waves 0..3 (group 0) and 4..7 (group 1) share the SIMDs pairwise.
+        // Each wave alternates a load phase (group 0 also issues the global
+        // loads of the next tile; then fragments of the whole current tile
+        // are read into registers) and a compute phase (all MFMAs of the
+        // tile).  Group 1 runs one phase behind group 0, so in every phase
+        // one wave per SIMD multiplies while the other loads.  Phases end
+        // with a workgroup barrier:
+        //   tile t in LDS  <- group 0 waits for its loads of tile t at the
+        //                     end of its compute phase of tile t-1;
+        //   stage reuse    <- group 1 reads tile t-1 in the phase before
+        //                     group 0 starts the loads of tile t+1 into it.
+        const int grp = wave >= NW / 2 ? 1 : 0;
+        const int lw = wave - grp * (NW / 2);
+        half8 fa[KSTEPS][MI], fb[KSTEPS][NI];
+        if (SCHED == 2) {
+            // Split ring: group 0 loads B one tile ahead (2 stages), group 1
+            // loads A two tiles ahead (3 stages), so each load phase carries
+            // half of a tile's traffic and every load has at least two
+            // phases to land.
+            //   B(t+1) lands <- group 0 waits at the end of its compute
+            //                   phase of tile t;
+            //   A(t+1) lands <- group 1 waits (leaving A(t+2) in flight) at
+            //                   the end of its load phase of tile t.
+            if (ktiles > 0) {
+                if (grp == 0) {
+                    issue_part(0, k_begin, lw, A_GROUPS, LOADS_PER_TILE);
+                } else {
+                    issue_part(0, k_begin, lw, 0, A_GROUPS);
+                    issue_part(1, k_begin + BK, lw, 0, A_GROUPS);
+                }
+                wait_vmcnt<0>();
+                block_sync();
+                if (grp == 1)
+                    block_sync();
+            }
+            int sa = 0, sb = 0;
+            for (int kt = 0; kt < ktiles; ++kt) {
+                // load phase
+                if (grp == 0)
+                    issue_part(sb ^ 1, k_begin + (int64_t)(kt + 1) * BK, lw,
+                               A_GROUPS, LOADS_PER_TILE);
+                else
+                    issue_part(sa == 0 ? 2 : sa - 1,
+                               k_begin + (int64_t)(kt + 2) * BK, lw, 0,
+                               A_GROUPS);
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    read_frags2(sa, sb, ks, fa[ks], fb[ks]);
+                wait_lgkmcnt<0>();
+                if (grp == 1)
+                    wait_vmcnt<A_GROUPS>();
+                block_sync();
+                // compute phase
+                __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+                for (int ks = 0; ks < KSTEPS; ++ks)
+                    mma(fa[ks], fb[ks]);
+                __builtin_amdgcn_s_setprio(0);
+                if (grp == 0)
+                    wait_vmcnt<0>();
+                block_sync();
+                sa = sa == 2 ? 0 : sa + 1;
+                sb ^= 1;
+            }
+            if (ktiles > 0 && grp == 0)
+                block_sync();
+            wait_vmcnt<0>();
         } else {
+        if (ktiles > 0) {
+            if (grp == 0)
+                issue_direct(0, k_begin, lw);
+            wait_vmcnt<0>();
+            block_sync();
+            if (grp == 1)
+                block_sync();
+        }
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int cur = kt & 1;
+            // load phase
+            if (grp == 0)
+                issue_direct(cur ^ 1, k_begin + (int64_t)(kt + 1) * BK, lw);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                read_frags(cur, ks, fa[ks], fb[ks]);
+            wait_lgkmcnt<0>();
+            block_sync();
+            // compute phase
+            __builtin_amdgcn_s_setprio(1);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks)
+                mma(fa[ks], fb[ks]);
+            __builtin_amdgcn_s_setprio(0);
+            if (grp == 0)
+                wait_vmcnt<0>();
+            block_sync();
+        }
+        if (ktiles > 0 && grp == 0)
+            block_sync();
+        }
+    } else if (LOADER == LOAD_DIRECT) {
+        // Tiles t .. t + STAGES - 1 are in LDS or in flight.  Fragments of
+        // k-step s + 1 are read while the MFMAs of k-step s run.  At the
+        // last k-step of tile t each wave waits for its own loads of tile
+        // t + 1 and passes the one barrier of the tile (after which no wave
+        // reads stage t % STAGES again and all of tile t + 1 is in LDS),
+        // then reads the first fragments of tile t + 1 while the last MFMAs
+        // of tile t are still in the pipe.
+        // With three or more stages the loads of tile t + STAGES - 1 go into
+        // the stage freed at the previous barrier and are spread over the
+        // k-steps of tile t (a burst of them stalls the issuing waves on the
+        // per-CU fill rate); with two stages they go, after the barrier,
+        // into the stage just freed.
+        constexpr bool SPREAD = STAGES >= 3;
+        constexpr int PER = SPREAD ? LOADS_PER_TILE / KSTEPS : 0;
+        static_assert(!SPREAD || PER * KSTEPS == LOADS_PER_TILE,
+                      "loads split evenly over the k-steps");
+        constexpr int PRO = SPREAD ? STAGES - 1 : STAGES;   // prologue tiles
+        constexpr int WAIT_N = SPREAD
+            ? (STAGES - 3) * LOADS_PER_TILE + (KSTEPS - 1) * PER
+            : (STAGES - 2) * LOADS_PER_TILE;
+        if (ktiles > 0) {
+#pragma unroll
+            for (int s = 0; s < PRO; ++s)
+                issue_direct(s, k_begin + (int64_t)s * BK, wave);
+            wait_vmcnt<(PRO - 1) * LOADS_PER_TILE>();
+            block_sync();
+        }
+        half8 fa[2][MI], fb[2][NI];
+        if (ktiles > 0)
+            read_frags(0, 0, fa[0], fb[0]);
+        int cur = 0;
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int refill = cur == 0 ? STAGES - 1 : cur - 1;
+            const int64_t k_refill = k_begin + (int64_t)(kt + STAGES - 1) * BK;
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS - 1; ++ks) {
+                __builtin_amdgcn_sched_barrier(0);
+                if (SPREAD)
+                    issue_part(refill, k_refill, wave, ks * PER,
+                               (ks + 1) * PER);
+                read_frags(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+                mma(fa[ks & 1], fb[ks & 1]);
+#pragma unroll
+                for (int x = 0; x < MFMAS; ++x) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    if (x < FRAGS)
+                        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    if (x < PER)
+                        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+            constexpr int LAST = (KSTEPS - 1) & 1;
+            constexpr int LAST_LOADS = SPREAD ? PER : LOADS_PER_TILE;
+            const int nxt = cur + 1 == STAGES ? 0 : cur + 1;
+            wait_vmcnt<WAIT_N>();
+            wait_lgkmcnt<0>();
+            block_sync();
+            if (SPREAD)
+                issue_part(refill, k_refill, wave, (KSTEPS - 1) * PER,
+                           LOADS_PER_TILE);
+            else
+                issue_direct(cur, k_begin + (int64_t)(kt + STAGES) * BK, wave);
+            read_frags(nxt, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+            mma(fa[LAST], fb[LAST]);
+#pragma unroll
+            for (int x = 0; x < MFMAS; ++x) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                if (x < FRAGS)
+                    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                if (x < LAST_LOADS)
+                    __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            cur = nxt;
+        }
+        wait_vmcnt<0>();
+    } else {
+        if (ktiles > 0) {
             fetch_regs(k_begin);
             store_regs(0);
         }
-    }
-    for (int kt = 0; kt < ktiles; ++kt) {
-        const int cur = kt & 1;
-        if (LOADER == LOAD_DIRECT)
-            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        __syncthreads();
-        const bool more = kt + 1 < ktiles;
-        const int64_t k_next = k_begin + (int64_t)(kt + 1) * BK;
-        if (more) {
-            if (LOADER == LOAD_DIRECT)
-                issue_direct(cur ^ 1, k_next);
-            else
-                fetch_regs(k_next);
+        for (int kt = 0; kt < ktiles; ++kt) {
+            const int cur = kt & 1;
+            __syncthreads();
+            const bool more = kt + 1 < ktiles;
+            if (more)
+                fetch_regs(k_begin + (int64_t)(kt + 1) * BK);
+#pragma unroll
+            for (int ks = 0; ks < KSTEPS; ++ks) {
+                half8 af[MI], bf[NI];
+                read_frags(cur, ks, af, bf);
+                mma(af, bf);
+            }
+            if (more)
+                store_regs(cur ^ 1);
         }
-        compute(cur);
-        if (LOADER != LOAD_DIRECT && more)
-            store_regs(cur ^ 1);
     }
 
     // ---- epilogue --------------------------------------------------------
     // Accumulator block (i, j), register 4g + e of lane l holds
     //   m = m0 + wm*WTM + i*32 + (l % 32)
     //   n = n0 + wn*WTN + j*32 + 8g + 4(l / 32) + e.
+    // Each lane therefore owns 4 consecutive n of 32 different rows; stored
+    // straight from registers every instruction would touch 32 rows with a
+    // few bytes each.  Instead every wave turns its sub-tile around in its
+    // own slice of LDS (free once the main loop is done) and writes whole
+    // 256-byte row segments with 16-byte stores.
     const int em = lane & 31;
-    const int en = (lane >> 5) * 4;
+    const int eh = lane >> 5;
+    const int en = eh * 4;
+    constexpr int ES = SPLIT ? 4 : OutTraits<OutT>::bytes;
+    constexpr int LDS_BYTES = LDS_HALVES * 2;
+    constexpr int REGION = LDS_BYTES / NW;            // bytes per wave
+    constexpr int ROW_BYTES = WTN * ES;
+    constexpr int CPR = ROW_BYTES / 16;               // 16-byte chunks per row
+    constexpr int FIT = REGION / ROW_BYTES / 32 * 32;
+    constexpr int RPP = FIT < WTM ? FIT : WTM;        // rows per pass
+    constexpr int PASSES = WTM / RPP;
+    constexpr int LINE_ROWS = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
+    static_assert(RPP >= 32 && WTM % RPP == 0, "LDS slice holds 32-row bands");
+    static_assert(RPP * CPR % 64 == 0, "whole waves of 16-byte chunks");
+    // Chunk c of staged row r sits at chunk c ^ ((r / LINE_ROWS) % CPR'):
+    // the 32 rows a store instruction writes spread over distinct banks.
+    auto stage_chunk = [](int r, int c) {
+        constexpr int X = CPR < 16 ? CPR : 16;
+        return c ^ ((r / LINE_ROWS) % X);
+    };
+    char *region = (char *)lds + wave * REGION;
+
+    // Fp32 results of the block in output precision, then into the slice.
+    auto stage_pass = [&](int pass, auto finish) {
+#pragma unroll
+        for (int ii = 0; ii < RPP / 32; ++ii) {
+            const int i = pass * (RPP / 32) + ii;
+#pragma unroll
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
+                               acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
+                    v = finish(i, j, g, v);
+                    const int r = ii * 32 + em;
+                    const int col = j * 32 + 8 * g + en;      // element column
+                    const int cb = col * ES;                  // byte column
+                    char *dst = region + r * ROW_BYTES +
+                                stage_chunk(r, cb / 16) * 16 + cb % 16;
+                    if (ES == 4) {
+                        *(f32x4 *)dst = v;
+                    } else {
+                        half4 h = {(_Float16)v[0], (_Float16)v[1],
+                                   (_Float16)v[2], (_Float16)v[3]};
+                        *(half4 *)dst = h;
+                    }
+                }
+        }
+    };
+    // Slice rows back out, 16 bytes per lane, row-contiguous.
+    auto drain_pass = [&](int pass, __amdgpu_buffer_rsrc_t rOut, int64_t ld,
+                          int64_t n_limit) {
+#pragma unroll
+        for (int it = 0; it < RPP * CPR / 64; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx / CPR, c = idx % CPR;
+            const u32x4 v = *(const u32x4 *)(region + r * ROW_BYTES +
+                                             stage_chunk(r, c) * 16);
+            const int lm = wm * WTM + pass * RPP + r;
+            const int64_t n = n0 + wn * WTN + c * (16 / ES);
+            const uint32_t off =
+                n < n_limit ? (uint32_t)((lm * ld + n) * ES) : kOutOfRange;
+            __builtin_amdgcn_raw_buffer_store_b128(v, rOut, off, 0, 0);
+        }
+    };
+
+    const bool staged = SPLIT || VEC_OUT;
+    if (staged) {
+        // All waves are done with the pipeline's LDS (and its last loads).
+        wait_vmcnt<0>();
+        __syncthreads();
+    }
     if (SPLIT) {
         float *wsb = p.ws + ((int64_t)tc.s * p.batch + tc.b) * M * p.ws_ld +
                      m0 * p.ws_ld;
         const __amdgpu_buffer_rsrc_t rW =
             make_rsrc(wsb, (M - m0) * p.ws_ld * 4);
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
-#pragma unroll
-            for (int j = 0; j < NI; ++j)
-#pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int lm = wm * WTM + i * 32 + em;
-                    const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + en;
-                    const uint32_t off =
-                        n < N ? (uint32_t)((lm * p.ws_ld + n) * 4)
-                              : kOutOfRange;
-                    f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                               acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        __builtin_bit_cast(u32x4, v), rW, off, 0, 0);
-                }
+        for (int pass = 0; pass < PASSES; ++pass) {
+            stage_pass(pass, [](int, int, int, f32x4 v) { return v; });
+            drain_pass(pass, rW, p.ws_ld, N);
+        }
         return;
     }
 
-    constexpr int ES = OutTraits<OutT>::bytes;
     OutT *Db = (OutT *)p.D + tc.b * p.sD + m0 * N;
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(Db, (M - m0) * N * ES);
     const bool use_c = p.beta != 0.0f;
@@ -442,42 +793,64 @@ gemm_tn_kernel(GemmArgs p)
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(Cb, use_c ? (M - m0) * N * ES
                                                           : 0);
     const float alpha = p.alpha, beta = p.beta;
+
+    if (VEC_OUT) {
+        // alpha (and beta * C, read in the accumulator layout) in fp32, one
+        // rounding to the output type, then the coalesced write-out.
+        auto with_c = [&](int i, int j, int g, f32x4 v) {
+            const int lm = wm * WTM + i * 32 + em;
+            const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + en;
+            const uint32_t off =
+                n < N ? (uint32_t)((lm * N + n) * ES) : kOutOfRange;
+            const f32x4 c = load_out_vec4(rC, off, (OutT *)nullptr);
+            v = v * alpha;
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+            for (int e = 0; e < 4; ++e)
+                v[e] = __builtin_fmaf(beta, c[e], v[e]);
+            return v;
+        };
+        auto no_c = [&](int, int, int, f32x4 v) { return v * alpha; };
 #pragma unroll
-        for (int j = 0; j < NI; ++j)
+        for (int pass = 0; pass < PASSES; ++pass) {
+            if (use_c)
+                stage_pass(pass, with_c);
+            else
+                stage_pass(pass, no_c);
+            drain_pass(pass, rD, N, N);
+        }
+        return;
+    }
+
+    // Rows whose length or alignment rules out 16-byte stores: element by
+    // element, straight from the accumulators.
+    auto store_all = [&](auto with_c) {
+        constexpr bool WITH_C = decltype(with_c)::value;
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int lm = wm * WTM + i * 32 + em;
-                const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + en;
-                f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
-                           acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
-                v = v * alpha;
-                if (VEC_OUT) {
-                    const uint32_t off =
-                        n < N ? (uint32_t)((lm * N + n) * ES) : kOutOfRange;
-                    if (use_c) {
-                        f32x4 c = load_out_vec4(rC, off, (OutT *)nullptr);
+        for (int i = 0; i < MI; ++i)
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            v[e] = __builtin_fmaf(beta, c[e], v[e]);
-                    }
-                    store_out_vec4(rD, off, v, (OutT *)nullptr);
-                } else {
+            for (int j = 0; j < NI; ++j)
+#pragma unroll
+                for (int g = 0; g < 4; ++g) {
+                    const int lm = wm * WTM + i * 32 + em;
+                    const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + en;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t off =
                             n + e < N ? (uint32_t)((lm * N + n + e) * ES)
                                       : kOutOfRange;
-                        float x = v[e];
-                        if (use_c)
+                        float x = acc[i][j][4 * g + e] * alpha;
+                        if (WITH_C)
                             x = __builtin_fmaf(
                                 beta, load_out_elem(rC, off, (OutT *)nullptr),
                                 x);
                         store_out_elem(rD, off, x, (OutT *)nullptr);
                     }
                 }
-            }
+    };
+    if (use_c)
+        store_all(Bool<true>{});
+    else
+        store_all(Bool<false>{});
 }
 
 // ---------------------------------------------------------------------------

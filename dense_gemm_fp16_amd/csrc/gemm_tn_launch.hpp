@@ -5,9 +5,7 @@
 
 #include "gemm_tn_kernels.hpp"
 
-#ifndef GTN_SWZ
-#define GTN_SWZ 1   // LDS swizzle: chunk ^ ((row >> GTN_SWZ) & 7)
-#endif
+#include "gemm_tn_config.hpp"
 
 namespace gtn {
 
@@ -25,41 +23,43 @@ hipError_t launch_tile64(const GemmArgs &a, int loader, bool out_f32,
 hipError_t launch_splitk_reduce(const GemmArgs &a, bool out_f32,
                                 bool vec_out, hipStream_t s);
 
-template <int BM, int BN, int WM, int WN, int MINW, int LOADER>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int MINW, int SC,
+          int LOADER>
 void *pick_kernel(bool out_f32, bool split, bool vec_out)
 {
-    constexpr int S = GTN_SWZ;
     if (split)
-        return (void *)&gemm_tn_kernel<BM, BN, 64, WM, WN, S, LOADER, float,
-                                       true, true, MINW>;
+        return (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER, float,
+                                       true, true, MINW, SC>;
     if (out_f32)
-        return vec_out ? (void *)&gemm_tn_kernel<BM, BN, 64, WM, WN, S, LOADER,
-                                                 float, false, true, MINW>
-                       : (void *)&gemm_tn_kernel<BM, BN, 64, WM, WN, S, LOADER,
-                                                 float, false, false, MINW>;
-    return vec_out ? (void *)&gemm_tn_kernel<BM, BN, 64, WM, WN, S, LOADER,
-                                             _Float16, false, true, MINW>
-                   : (void *)&gemm_tn_kernel<BM, BN, 64, WM, WN, S, LOADER,
-                                             _Float16, false, false, MINW>;
+        return vec_out ? (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST,
+                                                 LOADER, float, false, true,
+                                                 MINW, SC>
+                       : (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST,
+                                                 LOADER, float, false, false,
+                                                 MINW, SC>;
+    return vec_out ? (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER,
+                                             _Float16, false, true, MINW, SC>
+                   : (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER,
+                                             _Float16, false, false, MINW, SC>;
 }
 
-template <int BM, int BN, int WM, int WN, int MINW>
+template <int BM, int BN, int BK, int WM, int WN, int ST, int MINW, int SC>
 hipError_t launch_tile(const GemmArgs &a, int loader, bool out_f32, bool split,
                        bool vec_out, unsigned grid, hipStream_t s)
 {
     void *fn;
     switch (loader) {
     case LOAD_DIRECT:
-        fn = pick_kernel<BM, BN, WM, WN, MINW, LOAD_DIRECT>(out_f32, split,
-                                                            vec_out);
+        fn = pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, LOAD_DIRECT>(
+            out_f32, split, vec_out);
         break;
     case LOAD_VREG:
-        fn = pick_kernel<BM, BN, WM, WN, MINW, LOAD_VREG>(out_f32, split,
-                                                          vec_out);
+        fn = pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, LOAD_VREG>(
+            out_f32, split, vec_out);
         break;
     default:
-        fn = pick_kernel<BM, BN, WM, WN, MINW, LOAD_ELEM>(out_f32, split,
-                                                          vec_out);
+        fn = pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, LOAD_ELEM>(
+            out_f32, split, vec_out);
         break;
     }
     GemmArgs copy = a;

@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include "gemm_tn.h"
+#include "gemm_tn_config.hpp"
 
 namespace gtn {
 
@@ -18,7 +19,10 @@ enum { PLAN_LOAD_DIRECT = 0, PLAN_LOAD_VREG = 1, PLAN_LOAD_ELEM = 2 };
 enum { TILE_256 = 0, TILE_128 = 1, TILE_64 = 2, NUM_TILES = 3 };
 
 constexpr int kTileDim[NUM_TILES] = {256, 128, 64};
-constexpr int kBK = 64;
+constexpr int kTileBK[NUM_TILES] = {GTN_T256_BK, GTN_T128_BK, GTN_T64_BK};
+constexpr int kTileStages[NUM_TILES] = {GTN_T256_STAGES, GTN_T128_STAGES,
+                                        GTN_T64_STAGES};
+constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
 // Addressing limits: the kernels form 32-bit byte offsets relative to the
@@ -29,7 +33,7 @@ constexpr int64_t kMaxN = int64_t(1) << 20;
 constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
 
 // Vector loader used when alignment allows it.
-constexpr int kDefaultVecLoader = PLAN_LOAD_VREG;
+constexpr int kDefaultVecLoader = PLAN_LOAD_DIRECT;
 
 struct Plan {
     int status = GEMM_TN_OK;
@@ -138,8 +142,8 @@ inline Override parse_override(const char *s)
 }
 
 // Choose the kernel configuration.  vec_in: A and B 16-byte aligned, K and
-// the A/B batch strides multiples of 8.  vec_out: C (when read) and D
-// aligned to 4 elements, N and the C/D batch strides multiples of 4.
+// the A/B batch strides multiples of 8.  vec_out: every row of D (and of C
+// when it is read) starts on a 16-byte boundary.
 inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
                       int64_t sA, int64_t sB, int64_t sC, int64_t sD,
                       int d_dtype, bool vec_in, bool vec_out,
@@ -229,9 +233,10 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
         return p.status;
     }
     snprintf(buf, (size_t)buflen,
-             "tile=%dx%dx%d waves=2x2 loader=%s split=%d k_split=%lld "
-             "vec_out=%d group_m=%d grid=%lld",
-             p.bm, p.bn, kBK, loaders[p.loader], p.splits,
+             "tile=%dx%dx%d stages=%d waves=2x2 loader=%s split=%d "
+             "k_split=%lld vec_out=%d group_m=%d grid=%lld",
+             p.bm, p.bn, kTileBK[p.tile], kTileStages[p.tile],
+             loaders[p.loader], p.splits,
              (long long)p.k_split, p.vec_out ? 1 : 0, p.group_m,
              (long long)p.grid);
     return p.status;

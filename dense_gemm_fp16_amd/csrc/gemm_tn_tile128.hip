@@ -1,4 +1,4 @@
-// Instantiations of the 128x128x64 tile (2 x 2 waves).
+// Instantiations of the 128x128 tile (2 x 2 waves).
 #include "gemm_tn_launch.hpp"
 
 namespace gtn {
@@ -7,8 +7,8 @@ hipError_t launch_tile128(const GemmArgs &a, int loader, bool out_f32,
                          bool split, bool vec_out, unsigned grid,
                          hipStream_t s)
 {
-    return launch_tile<128, 128, 2, 2, 2>(a, loader, out_f32, split, vec_out,
-                                          grid, s);
+    return launch_tile<128, 128, GTN_T128_BK, 2, 2, GTN_T128_STAGES, 2, 0>(
+        a, loader, out_f32, split, vec_out, grid, s);
 }
 
 }  // namespace gtn

@@ -1,4 +1,4 @@
-// Instantiations of the 256x256x64 tile (2 x 2 waves).
+// Instantiations of the 256x256 tile.
 #include "gemm_tn_launch.hpp"
 
 namespace gtn {
@@ -7,8 +7,9 @@ hipError_t launch_tile256(const GemmArgs &a, int loader, bool out_f32,
                          bool split, bool vec_out, unsigned grid,
                          hipStream_t s)
 {
-    return launch_tile<256, 256, 2, 2, 1>(a, loader, out_f32, split, vec_out,
-                                          grid, s);
+    return launch_tile<256, 256, GTN_T256_BK, GTN_T256_WM, GTN_T256_WN,
+                       GTN_T256_STAGES, GTN_T256_MINW, GTN_T256_SCHED>(
+        a, loader, out_f32, split, vec_out, grid, s);
 }
 
 }  // namespace gtn

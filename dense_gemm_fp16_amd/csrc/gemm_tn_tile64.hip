@@ -1,4 +1,4 @@
-// Instantiations of the 64x64x64 tile (2 x 2 waves).
+// Instantiations of the 64x64 tile (2 x 2 waves).
 #include "gemm_tn_launch.hpp"
 
 namespace gtn {
@@ -7,8 +7,8 @@ hipError_t launch_tile64(const GemmArgs &a, int loader, bool out_f32,
                          bool split, bool vec_out, unsigned grid,
                          hipStream_t s)
 {
-    return launch_tile<64, 64, 2, 2, 2>(a, loader, out_f32, split, vec_out,
-                                          grid, s);
+    return launch_tile<64, 64, GTN_T64_BK, 2, 2, GTN_T64_STAGES, 2, 0>(
+        a, loader, out_f32, split, vec_out, grid, s);
 }
 
 }  // namespace gtn

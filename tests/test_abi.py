@@ -93,7 +93,7 @@ def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True):
 def test_plans_for_the_workloads():
     # 4096^3: one 256x256 tile per CU, vector loader, no split
     p = describe(1, 4096, 4096, 4096)
-    assert p["tile"] == "256x256x64" and p["split"] == "1"
+    assert p["tile"].startswith("256x256x") and p["split"] == "1"
     assert p["grid"] == "256" and p["loader"] != "elem"
     # 1024^3 and the ragged 1000x1030x1000: 64x64 tiles, enough of them
     assert describe(1, 1024, 1024, 1024, 0.5, "f32")["tile"] == "64x64x64"
@@ -105,7 +105,7 @@ def test_plans_for_the_workloads():
     assert int(p["split"]) * int(p["k_split"]) >= 8192
     # batched QK^T: 64 x (1024 x 1024 x 64)
     p = describe(64, 1024, 1024, 64, 0.0, "f32")
-    assert p["tile"] == "128x128x64" and int(p["grid"]) == 64 * 64
+    assert p["tile"].startswith("128x128x") and int(p["grid"]) == 64 * 64
     # K not a multiple of 8, or misaligned: element loader
     assert describe(1, 100, 100, 33)["loader"] == "elem"
     assert describe(1, 128, 128, 64, aligned=False)["loader"] == "elem"
@@ -115,7 +115,7 @@ def test_plans_for_the_workloads():
 def test_override_spec(monkeypatch):
     monkeypatch.setenv("GEMM_TN_FORCE", "tile=128,split=2,loader=0,group=2")
     p = describe(1, 512, 512, 1024)
-    assert p["tile"] == "128x128x64" and p["split"] == "2"
+    assert p["tile"].startswith("128x128x") and p["split"] == "2"
     assert p["loader"] == "direct" and p["group_m"] == "2"
     # a vector loader is refused when alignment does not allow it
     p = describe(1, 512, 512, 1000 + 3)

@@ -24,6 +24,84 @@ import numpy as np
 PEAK_F16_MFMA_TFLOPS = 2516.6   # 256 CU x 4096 FLOP/clk x 2.4 GHz, dense
 PEAK_HBM_GBS = 8000.0           # HBM3E
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILES = os.path.join(ROOT, "profiles")
+CSRC = os.path.join(ROOT, "dense_gemm_fp16_amd", "csrc")
+# device code of the GEMM kernels (host-side planning is not part of it)
+KERNEL_SOURCES = ("gemm_tn_kernels.hpp", "gemm_tn_config.hpp",
+                  "gemm_tn_launch.hpp", "gemm_tn_tile256.hip",
+                  "gemm_tn_tile128.hip", "gemm_tn_tile64.hip")
+
+
+def kernel_fingerprint() -> str:
+    """Hash of the kernel sources; a traffic figure measured on other
+    sources does not describe the kernel being timed."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(f.encode())
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_path(workload: str) -> str:
+    return os.path.join(PROFILES, f"gemm_tn_{workload}_traffic.json")
+
+
+def load_traffic(workload: str):
+    """HBM bytes per launch measured by the counters, if they were taken on
+    the current kernel sources; otherwise None."""
+    p = traffic_path(workload)
+    if not os.path.exists(p):
+        return None
+    t = json.load(open(p))
+    if t.get("fingerprint") != kernel_fingerprint():
+        return None
+    return t
+
+
+def summarize_pmc(fetch_csv, write_csv, workload, cal_mib):
+    """Per-launch HBM bytes of the GEMM kernel from FETCH_SIZE / WRITE_SIZE
+    (KiB per dispatch), each scaled by what the same counter reports for the
+    calibration copy of cal_mib MiB (which reads and writes cal_mib MiB)."""
+    import csv
+    import statistics
+
+    def per_kernel(path, counter):
+        gemm, copy = [], []
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            v = float(r["Counter_Value"])
+            name = r["Kernel_Name"]
+            if "gemm_tn_kernel" in name or "splitk_reduce" in name:
+                gemm.append((int(r["Dispatch_Id"]), name, v))
+            elif "copy" in name.lower():
+                copy.append(v)
+        return gemm, copy
+
+    out = {"workload": workload, "fingerprint": kernel_fingerprint(),
+           "calibration_mib": cal_mib}
+    for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
+                               ("write", write_csv, "WRITE_SIZE")):
+        gemm, copy = per_kernel(path, counter)
+        if not gemm or not copy:
+            raise SystemExit(f"{path}: no {counter} rows for the GEMM or "
+                             "the calibration copy")
+        cal_kib = max(copy)
+        factor = cal_mib * 1024.0 / cal_kib
+        # all kernels of one GEMM call (split-K adds a reduction) summed
+        names = sorted({n for _, n, _ in gemm})
+        per_name = {n: statistics.median(v for _, m, v in gemm if m == n)
+                    for n in names}
+        kib = sum(per_name.values())
+        out[f"{key}_kib_raw"] = kib
+        out[f"{key}_calibration_kib_raw"] = cal_kib
+        out[f"{key}_scale"] = factor
+        out[f"{key}_bytes"] = kib * 1024.0 * factor
+    out["bytes_per_launch"] = out["fetch_bytes"] + out["write_bytes"]
+    return out
+
 
 def _args():
     ap = argparse.ArgumentParser()
@@ -36,6 +114,16 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="run one device copy of this many MiB first (the "
+                         "known-size reference for HBM byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_CSV",
+                                                          "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc counter_collection.csv "
+                         "files (FETCH_SIZE, WRITE_SIZE) of a run with "
+                         "--copy-calibration-mib into a traffic summary")
+    ap.add_argument("--calibration-mib", type=int, default=256,
+                    help="size of the calibration copy in --summarize-pmc")
     return ap.parse_args()
 
 
@@ -108,6 +196,14 @@ def describe(w):
 
 def main():
     a = _args()
+    if a.summarize_pmc:
+        t = summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.workload,
+                          a.calibration_mib)
+        os.makedirs(PROFILES, exist_ok=True)
+        with open(traffic_path(a.workload), "w") as f:
+            json.dump(t, f, indent=1)
+        print(json.dumps(t))
+        return
     if a.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {a.gpus} is not "
               "supported (the GEMM runs on a single MI355X)", file=sys.stderr)
@@ -119,6 +215,13 @@ def main():
     import seeded_inputs as si
 
     w = si.workload(a.workload)
+    if a.copy_calibration_mib:
+        n = a.copy_calibration_mib * 1024 * 1024 // 4
+        src = torch.ones(n, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     sec = time_workload(w, a.steps, a.warmup)
     tflops = w.flops / sec / 1e12
     gbs = w.algorithmic_bytes / sec / 1e9
@@ -132,7 +235,8 @@ def main():
         roof = {"bound": "hbm", "achieved": round(gbs, 1),
                 "peak": PEAK_HBM_GBS, "unit": "GB/s",
                 "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = None
+    t = load_traffic(a.workload)
+    roof["traffic"] = round(t["bytes_per_launch"]) if t else None
     line = {
         "metric": "GEMM TFLOP/s (fp16 in, fp32 acc) at 4096^3; "
                   "% of MI355X fp16 MFMA peak",

@@ -22,6 +22,9 @@ constexpr int kTileDim[NUM_TILES] = {256, 128, 64};
 constexpr int kTileBK[NUM_TILES] = {GTN_T256_BK, GTN_T128_BK, GTN_T64_BK};
 constexpr int kTileStages[NUM_TILES] = {GTN_T256_STAGES, GTN_T128_STAGES,
                                         GTN_T64_STAGES};
+constexpr int kTileWM[NUM_TILES] = {GTN_T256_WM, 2, 2};
+constexpr int kTileWN[NUM_TILES] = {GTN_T256_WN, 2, 2};
+constexpr int kTileSched[NUM_TILES] = {GTN_T256_SCHED, 0, 0};
 constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
@@ -222,6 +225,7 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
 inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
 {
     static const char *loaders[] = {"direct", "vreg", "elem"};
+    static const char *scheds[] = {"interleaved", "pingpong", "pingpong-split"};
     if (buf == nullptr || buflen <= 0)
         return p.status;
     if (p.status != GEMM_TN_OK) {
@@ -233,9 +237,12 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
         return p.status;
     }
     snprintf(buf, (size_t)buflen,
-             "tile=%dx%dx%d stages=%d waves=2x2 loader=%s split=%d "
-             "k_split=%lld vec_out=%d group_m=%d grid=%lld",
+             "tile=%dx%dx%d stages=%d waves=%dx%d sched=%s loader=%s "
+             "split=%d k_split=%lld vec_out=%d group_m=%d grid=%lld",
              p.bm, p.bn, kTileBK[p.tile], kTileStages[p.tile],
+             kTileWM[p.tile], kTileWN[p.tile],
+             p.loader == PLAN_LOAD_DIRECT ? scheds[kTileSched[p.tile]]
+                                          : "staged",
              loaders[p.loader], p.splits,
              (long long)p.k_split, p.vec_out ? 1 : 0, p.group_m,
              (long long)p.grid);

@@ -1,6 +1,7 @@
-// Tile configurations: the k-depth BK and the LDS ring depth of each tile
-// shape.  Shared by the host planner and the kernel instantiations; the
-// macros exist so that tuning builds can try other values.
+// Tile configurations: the k-depth BK, the LDS ring depth and the MFMA
+// block edge of each tile shape.  Shared by the host planner and the kernel
+// instantiations; the macros exist so that tuning builds can try other
+// values.
 #pragma once
 
 #ifndef GTN_T256_BK
@@ -32,4 +33,13 @@
 #endif
 #ifndef GTN_T64_STAGES
 #define GTN_T64_STAGES 3
+#endif
+#ifndef GTN_T256_MFMA
+#define GTN_T256_MFMA 16
+#endif
+#ifndef GTN_T128_MFMA
+#define GTN_T128_MFMA 16
+#endif
+#ifndef GTN_T64_MFMA
+#define GTN_T64_MFMA 16
 #endif

@@ -20,11 +20,12 @@
 //    rows over distinct banks (page "cute(8) smem_gemm", section 3:
 //    Swizzle<B,M,S> XORs the row bits into the group index); f is chosen
 //    for gfx950's 64-bank LDS (see swizzle_chunk).
-//  * LDS -> registers: v_mfma_f32_32x32x16_f16 takes, in each lane, 8
-//    consecutive-k halves of one row of each operand; in TN storage that is
-//    one ds_read_b128 per operand per lane, with no shuffle.
-//  * MFMA: each wave owns a (BM/WM) x (BN/WN) sub-tile as a grid of 32 x 32
-//    fp32 accumulator blocks.  The operands are issued as (B, A), so the
+//  * LDS -> registers: v_mfma_f32_16x16x32_f16 (and 32x32x16) takes, in
+//    each lane, 8 consecutive-k halves of one row of each operand; in TN
+//    storage that is one ds_read_b128 per operand per lane, with no
+//    shuffle.
+//  * MFMA: each wave owns a (BM/WM) x (BN/WN) sub-tile as a grid of 16 x 16
+//    (or 32 x 32) fp32 accumulator blocks.  The operands are issued as (B, A), so the
 //    accumulator block is D^T: each lane then holds 4 consecutive n of one
 //    m per group of 4 registers, which the epilogue stores as one 8- or
 //    16-byte vector.
@@ -139,10 +140,6 @@ template <bool V>
 struct Bool {
     static constexpr bool value = V;
 };
-template <int V>
-struct Int {
-    static constexpr int value = V;
-};
 
 // s_waitcnt with only the vector-memory counter (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
@@ -255,13 +252,17 @@ __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 //           registers while the other issues loads and fragment reads);
 //           2 = ping-pong with the tile loads split between the two wave
 //           groups (A ring of three stages, B ring of two);
+//   MB : MFMA block edge, 32 (v_mfma_f32_32x32x16_f16) or 16
+//        (v_mfma_f32_16x16x32_f16: the same work per cycle, in four times as
+//        many instructions, at a lower power per flop on random data);
 //   OutT : _Float16 or float; SPLIT : write fp32 partials to the workspace;
 //   VEC_OUT : rows of D (and C) start on 16-byte boundaries (N * element
 //             size a multiple of 16, D / C 16-byte aligned): the tile is
 //             written through LDS with 16-byte stores.
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADER,
-          typename OutT, bool SPLIT, bool VEC_OUT, int MIN_WAVES, int SCHED>
+          typename OutT, bool SPLIT, bool VEC_OUT, int MIN_WAVES, int SCHED,
+          int MB>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64,
                                                            WM * WN * 64),
                                amdgpu_waves_per_eu(MIN_WAVES, 8)))
@@ -270,14 +271,23 @@ gemm_tn_kernel(GemmArgs p)
     constexpr int NW = WM * WN;
     constexpr int NT = NW * 64;
     constexpr int WTM = BM / WM, WTN = BN / WN;
-    constexpr int MI = WTM / 32, NI = WTN / 32;
-    constexpr int KSTEPS = BK / 16;
+    static_assert(MB == 32 || MB == 16, "MFMA blocks of 32x32 or 16x16");
+    constexpr int MI = WTM / MB, NI = WTN / MB;
+    // A fragment: lane l holds 8 consecutive k of row l % MB, at k offset
+    // 8 * (l / MB) of a KM-wide k-step; QN lanes groups cover the k-step.
+    constexpr int QN = 64 / MB;
+    constexpr int KM = 8 * QN;
+    constexpr int KSTEPS = BK / KM;
+    // Accumulator registers per block, in groups of 4 consecutive n.
+    constexpr int ACC = MB * MB / 64;
+    constexpr int G = ACC / 4;
     constexpr int CHUNKS = BK / 8;            // 16-byte chunks per tile row
     constexpr int ROWS_PER_WAVE_LOAD = 64 / CHUNKS;
     constexpr int STAGE_HALVES = (BM + BN) * BK;
     static_assert(BK == 32 || BK == 64, "tile rows of 64 or 128 bytes");
     static_assert(STAGES >= 2, "at least double buffering");
-    static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile of 32x32 blocks");
+    static_assert(WTM % MB == 0 && WTN % MB == 0, "wave tile of MFMA blocks");
+    static_assert(BK % KM == 0, "whole k-steps per tile");
     static_assert(BM % (ROWS_PER_WAVE_LOAD * NW) == 0 &&
                       BN % (ROWS_PER_WAVE_LOAD * NW) == 0,
                   "every wave issues the same number of tile loads");
@@ -322,12 +332,13 @@ gemm_tn_kernel(GemmArgs p)
     const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, (M - m0) * K * 2);
     const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bb, (N - n0) * K * 2);
 
-    f32x16 acc[MI][NI];
+    typedef float accv __attribute__((ext_vector_type(ACC)));
+    accv acc[MI][NI];
 #pragma unroll
     for (int i = 0; i < MI; ++i)
 #pragma unroll
         for (int j = 0; j < NI; ++j)
-            acc[i][j] = f32x16{};
+            acc[i][j] = accv{};
 
     // ---- global -> LDS ----------------------------------------------------
     // LOAD_DIRECT: one buffer_load_dwordx4 ... lds of a wave fills
@@ -442,9 +453,9 @@ gemm_tn_kernel(GemmArgs p)
         }
     };
 
-    // ---- LDS -> registers, and the MFMAs of one 16-wide k-step ---------
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
+    // ---- LDS -> registers, and the MFMAs of one KM-wide k-step ---------
+    const int frow = lane % MB;
+    const int fq = lane / MB;
     // Fragments are read in the order the MFMAs below consume them (B0, A0,
     // then B1.., then A1..), so the first MFMAs of a k-step depend only on
     // the oldest reads of the previous one.
@@ -452,14 +463,14 @@ gemm_tn_kernel(GemmArgs p)
                            half8 (&bf)[NI]) {
         const _Float16 *sA = lds + a_base(sta);
         const _Float16 *sB = lds + b_base(stb);
-        const int ch = ks * 2 + fhalf;
+        const int ch = ks * QN + fq;
         auto rd_a = [&](int i) {
-            const int row = wm * WTM + i * 32 + frow;
+            const int row = wm * WTM + i * MB + frow;
             af[i] = *(const half8 *)(sA + row * BK +
                                      swizzle_chunk<BK>(row, ch) * 8);
         };
         auto rd_b = [&](int j) {
-            const int row = wn * WTN + j * 32 + frow;
+            const int row = wn * WTN + j * MB + frow;
             bf[j] = *(const half8 *)(sB + row * BK +
                                      swizzle_chunk<BK>(row, ch) * 8);
         };
@@ -475,13 +486,18 @@ gemm_tn_kernel(GemmArgs p)
     auto read_frags = [&](int stage, int ks, half8 (&af)[MI], half8 (&bf)[NI]) {
         read_frags2(stage, stage, ks, af, bf);
     };
+    auto mfma = [](const half8 &b, const half8 &a, const accv &c) {
+        if constexpr (MB == 32)
+            return __builtin_amdgcn_mfma_f32_32x32x16_f16(b, a, c, 0, 0, 0);
+        else
+            return __builtin_amdgcn_mfma_f32_16x16x32_f16(b, a, c, 0, 0, 0);
+    };
     auto mma = [&](const half8 (&af)[MI], const half8 (&bf)[NI]) {
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
-                    bf[j], af[i], acc[i][j], 0, 0, 0);
+                acc[i][j] = mfma(bf[j], af[i], acc[i][j]);
     };
     // Instruction order inside one k-step (the compiler otherwise waits on
     // each fragment right before its first MFMA): the next k-step's
@@ -491,7 +507,7 @@ gemm_tn_kernel(GemmArgs p)
     constexpr int MFMAS = MI * NI;
 
     // ---- main loop -------------------------------------------------------
-    if (PINGPONG) {
+    if constexpr (PINGPONG) {
         // Waves 0..3 (group 0) and 4..7 (group 1) share the SIMDs pairwise.
         // Each wave alternates a load phase (group 0 also issues the global
         // loads of the next tile; then fragments of the whole current tile
@@ -591,7 +607,7 @@ gemm_tn_kernel(GemmArgs p)
         if (ktiles > 0 && grp == 0)
             block_sync();
         }
-    } else if (LOADER == LOAD_DIRECT) {
+    } else if constexpr (LOADER == LOAD_DIRECT) {
         // Tiles t .. t + STAGES - 1 are in LDS or in flight.  Fragments of
         // k-step s + 1 are read while the MFMAs of k-step s run.  At the
         // last k-step of tile t each wave waits for its own loads of tile
@@ -693,16 +709,15 @@ gemm_tn_kernel(GemmArgs p)
 
     // ---- epilogue --------------------------------------------------------
     // Accumulator block (i, j), register 4g + e of lane l holds
-    //   m = m0 + wm*WTM + i*32 + (l % 32)
-    //   n = n0 + wn*WTN + j*32 + 8g + 4(l / 32) + e.
-    // Each lane therefore owns 4 consecutive n of 32 different rows; stored
-    // straight from registers every instruction would touch 32 rows with a
+    //   m = m0 + wm*WTM + i*MB + (l % MB)
+    //   n = n0 + wn*WTN + j*MB + 4*QN*g + 4(l / MB) + e.
+    // Each lane therefore owns 4 consecutive n of MB different rows; stored
+    // straight from registers every instruction would touch MB rows with a
     // few bytes each.  Instead every wave turns its sub-tile around in its
     // own slice of LDS (free once the main loop is done) and writes whole
     // 256-byte row segments with 16-byte stores.
-    const int em = lane & 31;
-    const int eh = lane >> 5;
-    const int en = eh * 4;
+    const int em = lane % MB;
+    const int en = (lane / MB) * 4;
     constexpr int ES = SPLIT ? 4 : OutTraits<OutT>::bytes;
     constexpr int LDS_BYTES = LDS_HALVES * 2;
     constexpr int REGION = LDS_BYTES / NW;            // bytes per wave
@@ -715,7 +730,7 @@ gemm_tn_kernel(GemmArgs p)
     static_assert(RPP >= 32 && WTM % RPP == 0, "LDS slice holds 32-row bands");
     static_assert(RPP * CPR % 64 == 0, "whole waves of 16-byte chunks");
     // Chunk c of staged row r sits at chunk c ^ ((r / LINE_ROWS) % CPR'):
-    // the 32 rows a store instruction writes spread over distinct banks.
+    // the rows a store instruction writes spread over distinct banks.
     auto stage_chunk = [](int r, int c) {
         constexpr int X = CPR < 16 ? CPR : 16;
         return c ^ ((r / LINE_ROWS) % X);
@@ -725,17 +740,17 @@ gemm_tn_kernel(GemmArgs p)
     // Fp32 results of the block in output precision, then into the slice.
     auto stage_pass = [&](int pass, auto finish) {
 #pragma unroll
-        for (int ii = 0; ii < RPP / 32; ++ii) {
-            const int i = pass * (RPP / 32) + ii;
+        for (int ii = 0; ii < RPP / MB; ++ii) {
+            const int i = pass * (RPP / MB) + ii;
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
+                for (int g = 0; g < G; ++g) {
                     f32x4 v = {acc[i][j][4 * g], acc[i][j][4 * g + 1],
                                acc[i][j][4 * g + 2], acc[i][j][4 * g + 3]};
                     v = finish(i, j, g, v);
-                    const int r = ii * 32 + em;
-                    const int col = j * 32 + 8 * g + en;      // element column
+                    const int r = ii * MB + em;
+                    const int col = j * MB + 4 * QN * g + en;  // element column
                     const int cb = col * ES;                  // byte column
                     char *dst = region + r * ROW_BYTES +
                                 stage_chunk(r, cb / 16) * 16 + cb % 16;
@@ -798,8 +813,8 @@ gemm_tn_kernel(GemmArgs p)
         // alpha (and beta * C, read in the accumulator layout) in fp32, one
         // rounding to the output type, then the coalesced write-out.
         auto with_c = [&](int i, int j, int g, f32x4 v) {
-            const int lm = wm * WTM + i * 32 + em;
-            const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + en;
+            const int lm = wm * WTM + i * MB + em;
+            const int64_t n = n0 + wn * WTN + j * MB + 4 * QN * g + en;
             const uint32_t off =
                 n < N ? (uint32_t)((lm * N + n) * ES) : kOutOfRange;
             const f32x4 c = load_out_vec4(rC, off, (OutT *)nullptr);
@@ -830,9 +845,9 @@ gemm_tn_kernel(GemmArgs p)
 #pragma unroll
             for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int g = 0; g < 4; ++g) {
-                    const int lm = wm * WTM + i * 32 + em;
-                    const int64_t n = n0 + wn * WTN + j * 32 + 8 * g + en;
+                for (int g = 0; g < G; ++g) {
+                    const int lm = wm * WTM + i * MB + em;
+                    const int64_t n = n0 + wn * WTN + j * MB + 4 * QN * g + en;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const uint32_t off =

@@ -25,6 +25,8 @@ constexpr int kTileStages[NUM_TILES] = {GTN_T256_STAGES, GTN_T128_STAGES,
 constexpr int kTileWM[NUM_TILES] = {GTN_T256_WM, 2, 2};
 constexpr int kTileWN[NUM_TILES] = {GTN_T256_WN, 2, 2};
 constexpr int kTileSched[NUM_TILES] = {GTN_T256_SCHED, 0, 0};
+constexpr int kTileMfma[NUM_TILES] = {GTN_T256_MFMA, GTN_T128_MFMA,
+                                      GTN_T64_MFMA};
 constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
@@ -237,10 +239,12 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
         return p.status;
     }
     snprintf(buf, (size_t)buflen,
-             "tile=%dx%dx%d stages=%d waves=%dx%d sched=%s loader=%s "
-             "split=%d k_split=%lld vec_out=%d group_m=%d grid=%lld",
+             "tile=%dx%dx%d stages=%d waves=%dx%d mfma=%dx%d sched=%s "
+             "loader=%s split=%d k_split=%lld vec_out=%d group_m=%d "
+             "grid=%lld",
              p.bm, p.bn, kTileBK[p.tile], kTileStages[p.tile],
-             kTileWM[p.tile], kTileWN[p.tile],
+             kTileWM[p.tile], kTileWN[p.tile], kTileMfma[p.tile],
+             kTileMfma[p.tile],
              p.loader == PLAN_LOAD_DIRECT ? scheds[kTileSched[p.tile]]
                                           : "staged",
              loaders[p.loader], p.splits,

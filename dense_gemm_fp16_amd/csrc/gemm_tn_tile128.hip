@@ -7,7 +7,8 @@ hipError_t launch_tile128(const GemmArgs &a, int loader, bool out_f32,
                          bool split, bool vec_out, unsigned grid,
                          hipStream_t s)
 {
-    return launch_tile<128, 128, GTN_T128_BK, 2, 2, GTN_T128_STAGES, 2, 0>(
+    return launch_tile<128, 128, GTN_T128_BK, 2, 2, GTN_T128_STAGES, 2, 0,
+                       GTN_T128_MFMA>(
         a, loader, out_f32, split, vec_out, grid, s);
 }
 

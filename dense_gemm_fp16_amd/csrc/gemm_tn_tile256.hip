@@ -8,7 +8,8 @@ hipError_t launch_tile256(const GemmArgs &a, int loader, bool out_f32,
                          hipStream_t s)
 {
     return launch_tile<256, 256, GTN_T256_BK, GTN_T256_WM, GTN_T256_WN,
-                       GTN_T256_STAGES, GTN_T256_MINW, GTN_T256_SCHED>(
+                       GTN_T256_STAGES, GTN_T256_MINW, GTN_T256_SCHED,
+                       GTN_T256_MFMA>(
         a, loader, out_f32, split, vec_out, grid, s);
 }
 

@@ -7,7 +7,8 @@ hipError_t launch_tile64(const GemmArgs &a, int loader, bool out_f32,
                          bool split, bool vec_out, unsigned grid,
                          hipStream_t s)
 {
-    return launch_tile<64, 64, GTN_T64_BK, 2, 2, GTN_T64_STAGES, 2, 0>(
+    return launch_tile<64, 64, GTN_T64_BK, 2, 2, GTN_T64_STAGES, 2, 0,
+                       GTN_T64_MFMA>(
         a, loader, out_f32, split, vec_out, grid, s);
 }
 

@@ -32,7 +32,7 @@
 #define GTN_T64_BK 64
 #endif
 #ifndef GTN_T64_STAGES
-#define GTN_T64_STAGES 3
+#define GTN_T64_STAGES 4
 #endif
 #ifndef GTN_T256_MFMA
 #define GTN_T256_MFMA 16
@@ -42,4 +42,9 @@
 #endif
 #ifndef GTN_T64_MFMA
 #define GTN_T64_MFMA 16
+#endif
+// Cache-policy bits of the staged 16-byte output stores (gfx950: 1 = sc0,
+// 2 = nt, 16 = sc1).
+#ifndef GTN_STORE_CPOL
+#define GTN_STORE_CPOL 2
 #endif

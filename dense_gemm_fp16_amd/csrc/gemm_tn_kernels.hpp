@@ -44,6 +44,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm_tn_config.hpp"
+
 namespace gtn {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
@@ -620,6 +622,8 @@ gemm_tn_kernel(GemmArgs p)
         // k-steps of tile t (a burst of them stalls the issuing waves on the
         // per-CU fill rate); with two stages they go, after the barrier,
         // into the stage just freed.
+        static_assert(KSTEPS % 2 == 0,
+                      "fragment double buffer returns to slot 0 each tile");
         constexpr bool SPREAD = STAGES >= 3;
         constexpr int PER = SPREAD ? LOADS_PER_TILE / KSTEPS : 0;
         static_assert(!SPREAD || PER * KSTEPS == LOADS_PER_TILE,
@@ -777,7 +781,8 @@ gemm_tn_kernel(GemmArgs p)
             const int64_t n = n0 + wn * WTN + c * (16 / ES);
             const uint32_t off =
                 n < n_limit ? (uint32_t)((lm * ld + n) * ES) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rOut, off, 0, 0);
+            __builtin_amdgcn_raw_buffer_store_b128(v, rOut, off, 0,
+                                                   GTN_STORE_CPOL);
         }
     };
 

@@ -264,3 +264,37 @@ def test_fp16_overflow_rounds_to_inf():
     B = torch.full((32, K), 30.0, dtype=torch.float16, device="cuda")
     D = g.gemm_tn(A, B, out_dtype=torch.float16)   # 76800 > 65504
     assert torch.isinf(D).all() and (D > 0).all()
+
+
+def test_split_k_workspace_reuse(monkeypatch):
+    """The split-K workspace is kept per stream and grown on demand: calls
+    with more and fewer tiles, alternating between two streams, with C
+    aliasing D, all stay exact."""
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=64,split=4")
+    side = torch.cuda.Stream()
+    shapes = [(1, 130, 200, 1024, "f32", 0.0), (2, 256, 320, 1100, "f16", 0.5),
+              (1, 64, 64, 2048, "f32", -1.0), (3, 200, 136, 1024, "f32", 2.0),
+              (1, 130, 200, 1024, "f32", 0.0)]
+    for rep, (batch, M, N, K, out, beta) in enumerate(shapes):
+        w = _int_workload(batch, M, N, K, out, alpha=0.5, beta=beta)
+        stream = side if rep % 2 else torch.cuda.current_stream()
+        _say(f"[split workspace] {batch}x{M}x{N}x{K} {out} beta={beta} "
+             f"stream={'side' if rep % 2 else 'current'}")
+        A = torch.from_numpy(w.A).cuda()
+        B = torch.from_numpy(w.B).cuda()
+        dt = torch.float16 if out == "f16" else torch.float32
+        CD = (torch.from_numpy(w.C.copy()).cuda() if w.C is not None
+              else torch.zeros(batch, M, N, dtype=dt, device="cuda"))
+        torch.cuda.synchronize()
+        st = g.gemm_tn_strided_batched(
+            batch, M, N, K, w.alpha, A.data_ptr(), M * K, B.data_ptr(), N * K,
+            w.beta, CD.data_ptr() if beta != 0.0 else None, M * N,
+            CD.data_ptr(), M * N,
+            g.GEMM_TN_F16 if out == "f16" else g.GEMM_TN_F32,
+            stream.cuda_stream)
+        assert st == g.OK
+        torch.cuda.synchronize()
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(CD.cpu().numpy(), ref, out)
+        assert res.ok, f"{batch}x{M}x{N}x{K}: {res}"

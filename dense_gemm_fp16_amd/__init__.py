@@ -8,7 +8,11 @@ library is missing, importing the package raises ImportError.
     D = gemm_tn(A, B, alpha=1.0, beta=0.0, C=None, out_dtype=torch.float16)
 
 A: (M, K) or (batch, M, K) float16, B: (N, K) or (batch, N, K) float16,
-both contiguous on the GPU; C / D: (M, N) or (batch, M, N) of out_dtype.
+C / D: (M, N) or (batch, M, N) of out_dtype, all on the GPU.  Each matrix
+must be row-major with unit element stride; its row stride (leading
+dimension) and batch stride are taken from the tensor, so row slices of a
+wider array (and, for A and B, a batch dimension made by expand) are
+accepted without a copy.
 """
 from __future__ import annotations
 
@@ -27,12 +31,19 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(5)
 # launches then go through one runtime.
 import torch  # noqa: E402,F401
 
+EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_ex",
+           "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version")
+
+_REBUILD = ("run `python dense_gemm_fp16_amd/build.py` "
+            "(or __graft_entry__.build()) first")
 if not os.path.exists(LIB_PATH):
-    raise ImportError(
-        f"{LIB_PATH} is not built; run `python -m dense_gemm_fp16_amd.build` "
-        "(or __graft_entry__.build()) first")
+    raise ImportError(f"{LIB_PATH} is not built; {_REBUILD}")
 
 _lib = ctypes.CDLL(LIB_PATH)
+_missing = [n for n in EXPORTS if not hasattr(_lib, n)]
+if _missing:
+    raise ImportError(f"{LIB_PATH} is stale (no {', '.join(_missing)}); "
+                      f"{_REBUILD}")
 _i64, _f32, _vp, _int = (ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
                          ctypes.c_int)
 _lib.gemm_tn.restype = _int
@@ -42,17 +53,19 @@ _lib.gemm_tn_strided_batched.restype = _int
 _lib.gemm_tn_strided_batched.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp,
                                          _i64, _vp, _i64, _f32, _vp, _i64,
                                          _vp, _i64, _int, _vp]
+_lib.gemm_tn_ex.restype = _int
+_lib.gemm_tn_ex.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp, _i64, _i64,
+                            _vp, _i64, _i64, _f32, _vp, _i64, _i64, _vp, _i64,
+                            _i64, _int, _vp]
 _lib.gemm_tn_describe.restype = _int
 _lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
-                                  _i64, _f32, _int, _int, ctypes.c_char_p,
-                                  _i64]
+                                  _i64, _i64, _i64, _i64, _i64, _f32, _int,
+                                  _int, ctypes.c_char_p, _i64]
 _lib.gemm_tn_status_string.restype = ctypes.c_char_p
 _lib.gemm_tn_status_string.argtypes = [_int]
 _lib.gemm_tn_version.restype = _int
 _lib.gemm_tn_version.argtypes = []
 
-EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_describe",
-           "gemm_tn_status_string", "gemm_tn_version")
 
 
 class GemmError(RuntimeError):
@@ -77,12 +90,15 @@ def lib() -> ctypes.CDLL:
 
 
 def describe(batch, M, N, K, beta=0.0, out_dtype="f16", aligned16=True,
-             strides=None) -> str:
-    """Kernel configuration the library picks for this problem."""
+             strides=None, lds=None) -> str:
+    """Kernel configuration the library picks for this problem.
+    lds = (lda, ldb, ldc, ldd), packed rows by default."""
+    if lds is None:
+        lds = (K, K, N, N)
     if strides is None:
-        strides = (M * K, N * K, M * N, M * N)
+        strides = (M * lds[0], N * lds[1], M * lds[2], M * lds[3])
     buf = ctypes.create_string_buffer(256)
-    _lib.gemm_tn_describe(batch, M, N, K, *strides, float(beta),
+    _lib.gemm_tn_describe(batch, M, N, K, *lds, *strides, float(beta),
                           GEMM_TN_F16 if out_dtype == "f16" else GEMM_TN_F32,
                           1 if aligned16 else 0, buf, len(buf))
     return buf.value.decode()
@@ -112,10 +128,23 @@ def _check_operand(t, name):
     torch = _torch()
     if t.dtype != torch.float16:
         raise TypeError(f"{name} must be float16")
+    _check_layout(t, name)
+
+
+def _check_layout(t, name):
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous (row-major)")
+    if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+        raise ValueError(f"{name} must be row-major with unit element stride")
+
+
+def _ld(t):
+    """Row stride of a 2-D matrix or of each matrix of a 3-D batch."""
+    return t.stride(-2) if t.shape[-2] > 1 else max(t.shape[-1], 1)
+
+
+def _bstride(t):
+    return t.stride(0) if t.dim() == 3 else 0
 
 
 def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
@@ -146,21 +175,22 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
         dt = out_dtype if out_dtype is not None else (
             C.dtype if C is not None else torch.float16)
         out = torch.empty(shape, dtype=dt, device=A.device)
-    if tuple(out.shape) != shape or not out.is_contiguous() or not out.is_cuda:
-        raise ValueError(f"out must be a contiguous GPU tensor of shape {shape}")
+    if tuple(out.shape) != shape:
+        raise ValueError(f"out must have shape {shape}")
+    _check_layout(out, "out")
     code = _dtype_code(out.dtype)
-    c_ptr = None
+    c_ptr, ldc, sc = None, N, 0
     if beta != 0.0:
         if C is None:
             raise ValueError("beta != 0 needs C")
-        if (tuple(C.shape) != shape or C.dtype != out.dtype
-                or not C.is_contiguous() or not C.is_cuda):
-            raise ValueError("C must match D's shape and dtype, contiguous")
-        c_ptr = C.data_ptr()
-    st = _lib.gemm_tn_strided_batched(
-        batch, M, N, K, float(alpha), A.data_ptr(), M * K, B.data_ptr(),
-        N * K, float(beta), c_ptr, M * N, out.data_ptr(), M * N, code,
-        _stream_handle(stream))
+        if tuple(C.shape) != shape or C.dtype != out.dtype:
+            raise ValueError("C must match D's shape and dtype")
+        _check_layout(C, "C")
+        c_ptr, ldc, sc = C.data_ptr(), _ld(C), _bstride(C)
+    st = _lib.gemm_tn_ex(
+        batch, M, N, K, float(alpha), A.data_ptr(), _ld(A), _bstride(A),
+        B.data_ptr(), _ld(B), _bstride(B), float(beta), c_ptr, ldc, sc,
+        out.data_ptr(), _ld(out), _bstride(out), code, _stream_handle(stream))
     if st != OK:
         raise GemmError(st)
     return out
@@ -181,3 +211,13 @@ def gemm_tn_raw(M, N, K, alpha, A_ptr, B_ptr, beta, C_ptr, D_ptr, d_dtype,
     """Raw-pointer call of gemm_tn(); returns the status code."""
     return _lib.gemm_tn(M, N, K, float(alpha), A_ptr, B_ptr, float(beta),
                         C_ptr, D_ptr, d_dtype, stream_handle)
+
+
+def gemm_tn_ex(batch, M, N, K, alpha, A_ptr, lda, strideA, B_ptr, ldb,
+               strideB, beta, C_ptr, ldc, strideC, D_ptr, ldd, strideD,
+               d_dtype, stream_handle) -> int:
+    """Raw-pointer call of gemm_tn_ex(); returns the status code."""
+    return _lib.gemm_tn_ex(batch, M, N, K, float(alpha), A_ptr, lda, strideA,
+                           B_ptr, ldb, strideB, float(beta), C_ptr, ldc,
+                           strideC, D_ptr, ldd, strideD, d_dtype,
+                           stream_handle)

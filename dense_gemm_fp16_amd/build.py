@@ -1,6 +1,8 @@
 """Build libgemm_tn.so (the HIP kernels and the C ABI) for gfx950 in-tree.
 
-    python -m dense_gemm_fp16_amd.build [--defines GTN_SWZ=0 ...]
+    python dense_gemm_fp16_amd/build.py [--defines GTN_T256_MFMA=32 ...]
+
+(run as a script: importing the package itself needs the built library).
 
 Each translation unit under csrc/ is compiled by hipcc in parallel, then
 linked into dense_gemm_fp16_amd/libgemm_tn.so.

@@ -74,12 +74,31 @@ bool aligned(const void *p, uintptr_t a)
     return ((uintptr_t)p % a) == 0;
 }
 
-int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
-        const void *A, int64_t sA, const void *B, int64_t sB, float beta,
-        const void *C, int64_t sC, void *D, int64_t sD, int d_dtype,
-        void *stream)
+// vec_in: 16-byte loads of A and B are possible; vec_out: 16-byte stores
+// of D (and loads of C) are.
+bool vector_inputs(bool aligned16, int64_t K, const Lds &ld, int64_t sA,
+                   int64_t sB)
 {
-    int st = check_sizes(batch, M, N, K, sA, sB, sC, sD, d_dtype);
+    return aligned16 && K % 8 == 0 && ld.a % 8 == 0 && ld.b % 8 == 0 &&
+           sA % 8 == 0 && sB % 8 == 0;
+}
+
+bool vector_outputs(bool d_aligned16, bool c_aligned16, int64_t N,
+                    const Lds &ld, int64_t sC, int64_t sD, float beta, int es)
+{
+    return d_aligned16 && (N * es) % 16 == 0 && (ld.d * es) % 16 == 0 &&
+           (sD * es) % 16 == 0 &&
+           (beta == 0.0f ||
+            (c_aligned16 && (ld.c * es) % 16 == 0 && (sC * es) % 16 == 0));
+}
+
+int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
+        const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb,
+        int64_t sB, float beta, const void *C, int64_t ldc, int64_t sC,
+        void *D, int64_t ldd, int64_t sD, int d_dtype, void *stream)
+{
+    const Lds ld{lda, ldb, ldc, ldd};
+    int st = check_sizes(batch, M, N, K, ld, sA, sB, sC, sD, d_dtype);
     if (st != GEMM_TN_OK)
         return st;
     if (batch == 0 || M == 0 || N == 0)
@@ -90,13 +109,12 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
 
     const bool out_f32 = d_dtype == GEMM_TN_F32;
     const int es = out_f32 ? 4 : 2;
-    const bool vec_in = aligned(A, 16) && aligned(B, 16) && K % 8 == 0 &&
-                        sA % 8 == 0 && sB % 8 == 0;
-    const bool vec_out = aligned(D, 16) && (N * es) % 16 == 0 &&
-                         (sD * es) % 16 == 0 &&
-                         (beta == 0.0f || (aligned(C, 16) && (sC * es) % 16 == 0));
-    const Plan p = make_plan(batch, M, N, K, sA, sB, sC, sD, d_dtype, vec_in,
-                             vec_out, getenv("GEMM_TN_FORCE"));
+    const bool vec_in =
+        vector_inputs(aligned(A, 16) && aligned(B, 16), K, ld, sA, sB);
+    const bool vec_out = vector_outputs(aligned(D, 16), aligned(C, 16), N, ld,
+                                        sC, sD, beta, es);
+    const Plan p = make_plan(batch, M, N, K, ld, sA, sB, sC, sD, d_dtype,
+                             vec_in, vec_out, getenv("GEMM_TN_FORCE"));
     if (p.status != GEMM_TN_OK)
         return p.status;
 
@@ -110,6 +128,10 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.M = M;
     a.N = N;
     a.K = K;
+    a.lda = lda;
+    a.ldb = ldb;
+    a.ldc = ldc;
+    a.ldd = ldd;
     a.sA = sA;
     a.sB = sB;
     a.sC = sC;
@@ -158,8 +180,8 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
             const void *B, float beta, const void *C, void *D, int d_dtype,
             void *stream)
 {
-    return gtn::run(1, M, N, K, alpha, A, 0, B, 0, beta, C, 0, D, 0, d_dtype,
-                    stream);
+    return gtn::run(1, M, N, K, alpha, A, K, 0, B, K, 0, beta, C, N, 0, D, N,
+                    0, d_dtype, stream);
 }
 
 int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -168,22 +190,33 @@ int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                             const void *C, int64_t strideC, void *D,
                             int64_t strideD, int d_dtype, void *stream)
 {
-    return gtn::run(batch, M, N, K, alpha, A, strideA, B, strideB, beta, C,
-                    strideC, D, strideD, d_dtype, stream);
+    return gtn::run(batch, M, N, K, alpha, A, K, strideA, B, K, strideB, beta,
+                    C, N, strideC, D, N, strideD, d_dtype, stream);
+}
+
+int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
+               const void *A, int64_t lda, int64_t strideA, const void *B,
+               int64_t ldb, int64_t strideB, float beta, const void *C,
+               int64_t ldc, int64_t strideC, void *D, int64_t ldd,
+               int64_t strideD, int d_dtype, void *stream)
+{
+    return gtn::run(batch, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
+                    beta, C, ldc, strideC, D, ldd, strideD, d_dtype, stream);
 }
 
 int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, int64_t ldd,
                      int64_t strideA, int64_t strideB, int64_t strideC,
                      int64_t strideD, float beta, int d_dtype, int aligned16,
                      char *buf, int64_t buflen)
 {
-    const bool vec_in = aligned16 && K % 8 == 0 && strideA % 8 == 0 &&
-                        strideB % 8 == 0;
+    const gtn::Lds ld{lda, ldb, ldc, ldd};
     const int es = d_dtype == GEMM_TN_F32 ? 4 : 2;
-    const bool vec_out = aligned16 && (N * es) % 16 == 0 &&
-                         (strideD * es) % 16 == 0 &&
-                         (beta == 0.0f || (strideC * es) % 16 == 0);
-    const gtn::Plan p = gtn::make_plan(batch, M, N, K, strideA, strideB,
+    const bool vec_in =
+        gtn::vector_inputs(aligned16 != 0, K, ld, strideA, strideB);
+    const bool vec_out = gtn::vector_outputs(aligned16 != 0, aligned16 != 0,
+                                             N, ld, strideC, strideD, beta, es);
+    const gtn::Plan p = gtn::make_plan(batch, M, N, K, ld, strideA, strideB,
                                        strideC, strideD, d_dtype, vec_in,
                                        vec_out, getenv("GEMM_TN_FORCE"));
     return gtn::describe_plan(p, buf, buflen);
@@ -207,6 +240,6 @@ const char *gemm_tn_status_string(int status)
     }
 }
 
-int gemm_tn_version(void) { return (1 << 16) | 0; }
+int gemm_tn_version(void) { return (1 << 16) | 1; }
 
 }  // extern "C"

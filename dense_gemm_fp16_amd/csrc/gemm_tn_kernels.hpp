@@ -72,7 +72,8 @@ struct GemmArgs {
     void *D;
     float *ws;          // split-K partials: [split][batch][M][ws_ld] fp32
     int64_t M, N, K;
-    int64_t sA, sB, sC, sD;   // batch strides in elements
+    int64_t lda, ldb, ldc, ldd;   // row strides in elements
+    int64_t sA, sB, sC, sD;       // batch strides in elements
     int64_t ws_ld;
     float alpha, beta;
     int tiles_m, tiles_n, batch, splits;
@@ -329,10 +330,15 @@ gemm_tn_kernel(GemmArgs p)
 
     // Operand resources start at the tile's first row; rows past M (N) lie
     // beyond the record count and read as zero.
-    const _Float16 *Ab = p.A + tc.b * p.sA + m0 * K;
-    const _Float16 *Bb = p.B + tc.b * p.sB + n0 * K;
-    const __amdgpu_buffer_rsrc_t rA = make_rsrc(Ab, (M - m0) * K * 2);
-    const __amdgpu_buffer_rsrc_t rB = make_rsrc(Bb, (N - n0) * K * 2);
+    const int64_t lda = p.lda, ldb = p.ldb;
+    const _Float16 *Ab = p.A + tc.b * p.sA + m0 * lda;
+    const _Float16 *Bb = p.B + tc.b * p.sB + n0 * ldb;
+    // The record count ends at the last row's K-th element: rows past M
+    // (N) start beyond it, so every element of theirs reads as zero.
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(Ab, ((M - m0 - 1) * lda + K) * 2);
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(Bb, ((N - n0 - 1) * ldb + K) * 2);
 
     typedef float accv __attribute__((ext_vector_type(ACC)));
     accv acc[MI][NI];
@@ -380,10 +386,13 @@ gemm_tn_kernel(GemmArgs p)
         const uint32_t kb = (uint32_t)(k0 < K ? k0 : K) * 2;
         const int row0 = lw * ROWS_PER_WAVE_LOAD + rrow;
         const int kc = swizzle_chunk<BK>(row0, pch) * 8;
-        const uint32_t lane_off = (uint32_t)(row0 * K + kc) * 2 + kb;
+        const uint32_t lane_off_a = (uint32_t)(row0 * lda + kc) * 2 + kb;
+        const uint32_t lane_off_b = (uint32_t)(row0 * ldb + kc) * 2 + kb;
         const bool valid = kc < rem;
-        const uint32_t group_stride =
-            (uint32_t)(NLOAD * ROWS_PER_WAVE_LOAD * K) * 2;
+        const uint32_t group_stride_a =
+            (uint32_t)(NLOAD * ROWS_PER_WAVE_LOAD * lda) * 2;
+        const uint32_t group_stride_b =
+            (uint32_t)(NLOAD * ROWS_PER_WAVE_LOAD * ldb) * 2;
 #pragma unroll
         for (int x = 0; x < LOADS_PER_TILE; ++x) {
             if (x < x0 || x >= x1)
@@ -391,7 +400,9 @@ gemm_tn_kernel(GemmArgs p)
             const bool isA = x < A_GROUPS;
             const int g = isA ? x : x - A_GROUPS;
             const uint32_t off =
-                valid ? lane_off + (uint32_t)g * group_stride : kOutOfRange;
+                !valid ? kOutOfRange
+                : isA  ? lane_off_a + (uint32_t)g * group_stride_a
+                       : lane_off_b + (uint32_t)g * group_stride_b;
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 isA ? rA : rB,
                 (GTN_LDS void *)(ldsp + (isA ? a_base(stage) : b_base(stage)) +
@@ -420,10 +431,11 @@ gemm_tn_kernel(GemmArgs p)
             const int row = (isA ? i * RB : i * RB - BM) + tid / CHUNKS;
             const int lch = tid % CHUNKS;
             const __amdgpu_buffer_rsrc_t r = isA ? rA : rB;
+            const int64_t ld = isA ? lda : ldb;
             const int64_t kk = k0 + lch * 8;
             if (LOADER == LOAD_VREG) {
                 const uint32_t off = kk < k_end
-                                         ? (uint32_t)((row * K + kk) * 2)
+                                         ? (uint32_t)((row * ld + kk) * 2)
                                          : kOutOfRange;
                 stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off,
                                                                       0, 0);
@@ -432,7 +444,7 @@ gemm_tn_kernel(GemmArgs p)
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const uint32_t off =
-                        kk + x < k_end ? (uint32_t)((row * K + kk + x) * 2)
+                        kk + x < k_end ? (uint32_t)((row * ld + kk + x) * 2)
                                        : kOutOfRange;
                     e[x] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
                 }
@@ -805,13 +817,15 @@ gemm_tn_kernel(GemmArgs p)
         return;
     }
 
-    OutT *Db = (OutT *)p.D + tc.b * p.sD + m0 * N;
-    const __amdgpu_buffer_rsrc_t rD = make_rsrc(Db, (M - m0) * N * ES);
+    const int64_t ldc = p.ldc, ldd = p.ldd;
+    OutT *Db = (OutT *)p.D + tc.b * p.sD + m0 * ldd;
+    const __amdgpu_buffer_rsrc_t rD =
+        make_rsrc(Db, ((M - m0 - 1) * ldd + N) * ES);
     const bool use_c = p.beta != 0.0f;
-    const OutT *Cb = use_c ? (const OutT *)p.C + tc.b * p.sC + m0 * N
+    const OutT *Cb = use_c ? (const OutT *)p.C + tc.b * p.sC + m0 * ldc
                            : (const OutT *)p.D;
-    const __amdgpu_buffer_rsrc_t rC = make_rsrc(Cb, use_c ? (M - m0) * N * ES
-                                                          : 0);
+    const __amdgpu_buffer_rsrc_t rC =
+        make_rsrc(Cb, use_c ? ((M - m0 - 1) * ldc + N) * ES : 0);
     const float alpha = p.alpha, beta = p.beta;
 
     if (VEC_OUT) {
@@ -821,7 +835,7 @@ gemm_tn_kernel(GemmArgs p)
             const int lm = wm * WTM + i * MB + em;
             const int64_t n = n0 + wn * WTN + j * MB + 4 * QN * g + en;
             const uint32_t off =
-                n < N ? (uint32_t)((lm * N + n) * ES) : kOutOfRange;
+                n < N ? (uint32_t)((lm * ldc + n) * ES) : kOutOfRange;
             const f32x4 c = load_out_vec4(rC, off, (OutT *)nullptr);
             v = v * alpha;
 #pragma unroll
@@ -836,7 +850,7 @@ gemm_tn_kernel(GemmArgs p)
                 stage_pass(pass, with_c);
             else
                 stage_pass(pass, no_c);
-            drain_pass(pass, rD, N, N);
+            drain_pass(pass, rD, ldd, N);
         }
         return;
     }
@@ -855,15 +869,20 @@ gemm_tn_kernel(GemmArgs p)
                     const int64_t n = n0 + wn * WTN + j * MB + 4 * QN * g + en;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        const uint32_t off =
-                            n + e < N ? (uint32_t)((lm * N + n + e) * ES)
-                                      : kOutOfRange;
+                        const bool in = n + e < N;
+                        const uint32_t offd =
+                            in ? (uint32_t)((lm * ldd + n + e) * ES)
+                               : kOutOfRange;
                         float x = acc[i][j][4 * g + e] * alpha;
-                        if (WITH_C)
+                        if (WITH_C) {
+                            const uint32_t offc =
+                                in ? (uint32_t)((lm * ldc + n + e) * ES)
+                                   : kOutOfRange;
                             x = __builtin_fmaf(
-                                beta, load_out_elem(rC, off, (OutT *)nullptr),
+                                beta, load_out_elem(rC, offc, (OutT *)nullptr),
                                 x);
-                        store_out_elem(rD, off, x, (OutT *)nullptr);
+                        }
+                        store_out_elem(rD, offd, x, (OutT *)nullptr);
                     }
                 }
     };
@@ -898,10 +917,10 @@ splitk_reduce_kernel(GemmArgs p)
         s = s + t;
     }
     constexpr int ES = OutTraits<OutT>::bytes;
-    OutT *Drow = (OutT *)p.D + b * p.sD + m * p.N;
+    OutT *Drow = (OutT *)p.D + b * p.sD + m * p.ldd;
     const __amdgpu_buffer_rsrc_t rD = make_rsrc(Drow, p.N * ES);
     const bool use_c = p.beta != 0.0f;
-    const OutT *Crow = use_c ? (const OutT *)p.C + b * p.sC + m * p.N
+    const OutT *Crow = use_c ? (const OutT *)p.C + b * p.sC + m * p.ldc
                              : (const OutT *)p.D;
     const __amdgpu_buffer_rsrc_t rC = make_rsrc(Crow, use_c ? p.N * ES : 0);
     f32x4 v = s * p.alpha;

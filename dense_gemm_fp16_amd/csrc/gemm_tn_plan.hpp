@@ -31,8 +31,9 @@ constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
 // Addressing limits: the kernels form 32-bit byte offsets relative to the
-// first row of a tile (at most 256 rows), so a row may hold at most 2^21
-// fp16 operand elements (K) or 2^20 output elements (N, fp32).
+// first row of a tile (at most 256 rows), so an operand row stride (and K)
+// may be at most 2^21 fp16 elements and an output row stride (and N) at
+// most 2^20 elements.
 constexpr int64_t kMaxK = int64_t(1) << 21;
 constexpr int64_t kMaxN = int64_t(1) << 20;
 constexpr int64_t kMaxM = (int64_t(1) << 31) - 1;
@@ -63,10 +64,18 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t *out)
     return !__builtin_mul_overflow(a, b, out);
 }
 
-// Size, stride and dtype checks (no pointers involved).
+// Leading dimensions (row strides, in elements) of the four matrices.
+struct Lds {
+    int64_t a, b, c, d;
+};
+
+inline Lds packed_lds(int64_t N, int64_t K) { return Lds{K, K, N, N}; }
+
+// Size, stride and dtype checks (no pointers involved).  Every row stride
+// is at least its row length; batches of D may not overlap.
 inline int check_sizes(int64_t batch, int64_t M, int64_t N, int64_t K,
-                       int64_t sA, int64_t sB, int64_t sC, int64_t sD,
-                       int d_dtype)
+                       const Lds &ld, int64_t sA, int64_t sB, int64_t sC,
+                       int64_t sD, int d_dtype)
 {
     if (batch < 0 || M < 0 || N < 0 || K < 0)
         return GEMM_TN_ERR_INVALID_ARG;
@@ -74,25 +83,45 @@ inline int check_sizes(int64_t batch, int64_t M, int64_t N, int64_t K,
         return GEMM_TN_ERR_INVALID_ARG;
     if (sA < 0 || sB < 0 || sC < 0 || sD < 0)
         return GEMM_TN_ERR_INVALID_ARG;
-    int64_t mk, nk, mn, t;
-    if (!mul_ok(M, K, &mk) || !mul_ok(N, K, &nk) || !mul_ok(M, N, &mn))
+    if (ld.a < K || ld.b < K || ld.c < N || ld.d < N)
         return GEMM_TN_ERR_INVALID_ARG;
-    if (!mul_ok(mn, 4, &t) || !mul_ok(mk, 2, &t) || !mul_ok(nk, 2, &t))
+    // Element extents of one matrix: (rows - 1) * ld + row length.
+    int64_t ea, eb, ed, t;
+    auto extent = [&](int64_t rows, int64_t l, int64_t len, int64_t *out) {
+        if (rows == 0 || len == 0) {
+            *out = 0;
+            return true;
+        }
+        return mul_ok(rows - 1, l, out) && !__builtin_add_overflow(*out, len, out);
+    };
+    if (!extent(M, ld.a, K, &ea) || !extent(N, ld.b, K, &eb) ||
+        !extent(M, ld.d, N, &ed) || !extent(M, ld.c, N, &t))
+        return GEMM_TN_ERR_INVALID_ARG;
+    if (ea > t)
+        t = ea;
+    if (eb > t)
+        t = eb;
+    if (ed > t)
+        t = ed;
+    if (!mul_ok(t, 4, &t))
         return GEMM_TN_ERR_INVALID_ARG;
     if (batch > 1) {
-        if (sD < mn)
+        if (sD < ed)
             return GEMM_TN_ERR_INVALID_ARG;  // batches of D would overlap
         const int64_t strides[4] = {sA, sB, sC, sD};
         for (int i = 0; i < 4; ++i) {
             int64_t span;
             if (!mul_ok(strides[i], batch - 1, &span) ||
-                !mul_ok(span + mn + mk + nk, 4, &t))
+                __builtin_add_overflow(span, ea + eb + ed, &span) ||
+                !mul_ok(span, 4, &span))
                 return GEMM_TN_ERR_INVALID_ARG;
         }
     }
     if (batch == 0 || M == 0 || N == 0)
         return GEMM_TN_OK;
     if (K > kMaxK || N > kMaxN || M > kMaxM)
+        return GEMM_TN_ERR_UNSUPPORTED;
+    if (ld.a > kMaxK || ld.b > kMaxK || ld.c > kMaxN || ld.d > kMaxN)
         return GEMM_TN_ERR_UNSUPPORTED;
     return GEMM_TN_OK;
 }
@@ -147,15 +176,16 @@ inline Override parse_override(const char *s)
 }
 
 // Choose the kernel configuration.  vec_in: A and B 16-byte aligned, K and
-// the A/B batch strides multiples of 8.  vec_out: every row of D (and of C
-// when it is read) starts on a 16-byte boundary.
+// the A/B row and batch strides multiples of 8.  vec_out: every row of D
+// (and of C when it is read) starts on a 16-byte boundary and holds a
+// whole number of 16-byte chunks.
 inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
-                      int64_t sA, int64_t sB, int64_t sC, int64_t sD,
-                      int d_dtype, bool vec_in, bool vec_out,
+                      const Lds &ld, int64_t sA, int64_t sB, int64_t sC,
+                      int64_t sD, int d_dtype, bool vec_in, bool vec_out,
                       const char *override_spec)
 {
     Plan p;
-    p.status = check_sizes(batch, M, N, K, sA, sB, sC, sD, d_dtype);
+    p.status = check_sizes(batch, M, N, K, ld, sA, sB, sC, sD, d_dtype);
     if (p.status != GEMM_TN_OK)
         return p;
     if (batch == 0 || M == 0 || N == 0) {

@@ -21,7 +21,11 @@
  *     round-to-nearest-even (fp16 overflow gives +-inf);
  *   - K == 0 gives D = beta*C (an empty sum); M == 0 or N == 0 is a no-op.
  *
- * Layout: every matrix is packed row-major (lda = ldb = K, ldc = ldd = N).
+ * Layout: every matrix is row-major.  gemm_tn and gemm_tn_strided_batched
+ * take packed rows (lda = ldb = K, ldc = ldd = N); gemm_tn_ex takes any row
+ * strides, as gemm_device takes a stride per matrix (page "gemm_device
+ * line-by-line walk-through", section 1: the global tensors are built from
+ * a pointer, a shape and the strides dA, dB, dC).
  * Element types: A and B are IEEE binary16; C and D share `d_dtype`.
  *
  * Ownership and asynchrony: the caller owns every buffer; they are device
@@ -59,10 +63,12 @@ typedef enum gemm_tn_dtype {
 typedef enum gemm_tn_status {
     GEMM_TN_OK = 0,
     GEMM_TN_ERR_INVALID_ARG = 1, /* negative size, NULL where data is needed,
-                                    bad dtype, overlapping batch strides,
-                                    size overflow */
+                                    bad dtype, a row stride shorter than its
+                                    row, overlapping batches of D, size
+                                    overflow */
     GEMM_TN_ERR_UNSUPPORTED = 2, /* sizes beyond the kernels' addressing
-                                    range: K > 2^22, N > 2^21 or
+                                    range: K or an A/B row stride > 2^21,
+                                    N or a C/D row stride > 2^20, or
                                     M > 2^31 - 1 */
     GEMM_TN_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
     GEMM_TN_ERR_WORKSPACE = 4    /* the split-K workspace could not be
@@ -104,12 +110,35 @@ int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                             int64_t strideD, int d_dtype, void *stream);
 
 /*
- * Name of the kernel configuration gemm_tn_strided_batched would launch for
- * this problem (tile shape, loader, split-K factor), written NUL-terminated
- * into buf (at most buflen bytes).  Pure host logic, no HIP call.  Returns
+ * The general form: gemm_tn_strided_batched with a row stride (leading
+ * dimension, in elements) per matrix, so that any row-major sub-matrix of
+ * a larger array can be an operand or the output:
+ *   A(m,k) = A[i*strideA + m*lda + k],   lda >= K
+ *   B(n,k) = B[i*strideB + n*ldb + k],   ldb >= K
+ *   C(m,n) = C[i*strideC + m*ldc + n],   ldc >= N
+ *   D(m,n) = D[i*strideD + m*ldd + n],   ldd >= N
+ * Only the M x N elements of each D are written; the ldd - N elements
+ * between rows are left untouched.  Batches of D must not overlap:
+ * strideD >= (M - 1)*ldd + N when batch > 1.  The 16-byte loaders need
+ * lda and ldb to be multiples of 8 as well (otherwise the element loader
+ * runs); 16-byte stores need ldd (and ldc when C is read) to keep rows on
+ * 16-byte boundaries.
+ */
+int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
+               const void *A, int64_t lda, int64_t strideA, const void *B,
+               int64_t ldb, int64_t strideB, float beta, const void *C,
+               int64_t ldc, int64_t strideC, void *D, int64_t ldd,
+               int64_t strideD, int d_dtype, void *stream);
+
+/*
+ * Name of the kernel configuration gemm_tn_ex would launch for this
+ * problem (tile shape, loader, split-K factor), written NUL-terminated
+ * into buf (at most buflen bytes).  aligned16 != 0 means every matrix
+ * pointer is 16-byte aligned.  Pure host logic, no HIP call.  Returns
  * GEMM_TN_OK or the status the GEMM call would return for these sizes.
  */
 int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
+                     int64_t lda, int64_t ldb, int64_t ldc, int64_t ldd,
                      int64_t strideA, int64_t strideB, int64_t strideC,
                      int64_t strideD, float beta, int d_dtype,
                      int aligned16, char *buf, int64_t buflen);
@@ -117,7 +146,7 @@ int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
 /* Human-readable text of a status code (static storage). */
 const char *gemm_tn_status_string(int status);
 
-/* Library ABI version: (major << 16) | minor. */
+/* Library ABI version: (major << 16) | minor (currently 1.1). */
 int gemm_tn_version(void);
 
 #ifdef __cplusplus

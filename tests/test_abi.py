@@ -36,7 +36,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g.version() == (1, 0)
+    assert g.version() == (1, 1)
     assert g.status_string(OK) == "ok"
     assert g.status_string(INVALID) == "invalid argument"
     assert g.status_string(99) == "unknown status"
@@ -85,8 +85,55 @@ def test_batched_argument_checks():
     assert batched(2 ** 40, 4, 4, 4, 2 ** 40, 16, 16, 16) == INVALID
 
 
-def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True):
-    d = g.describe(batch, M, N, K, beta, out, aligned)
+def ex(batch, M, N, K, lda, ldb, ldc, ldd, sA=0, sB=0, sC=0, sD=0,
+       beta=0.0, C=NULL, dt=F32):
+    return g.gemm_tn_ex(batch, M, N, K, 1.0, P, lda, sA, P, ldb, sB, beta, C,
+                        ldc, sC, P, ldd, sD, dt, S)
+
+
+@pytest.mark.parametrize("args,status", [
+    ((1, 4, 4, 8, 7, 8, 4, 4), INVALID),                  # lda < K
+    ((1, 4, 4, 8, 8, 7, 4, 4), INVALID),                  # ldb < K
+    ((1, 4, 4, 8, 8, 8, 4, 3), INVALID),                  # ldd < N
+    ((1, 4, 4, 8, 8, 8, 3, 4, 0, 0, 0, 0, 0.5, P), INVALID),  # ldc < N
+    ((1, 4, 4, 8, 2 ** 21 + 8, 8, 4, 4), UNSUPPORTED),    # lda too large
+    ((1, 4, 4, 8, 8, 8, 4, 2 ** 20 + 4), UNSUPPORTED),    # ldd too large
+    # batches of D: extent (M - 1) * ldd + N = 3 * 10 + 4 = 34
+    ((2, 4, 4, 8, 8, 8, 4, 10, 0, 0, 0, 33), INVALID),
+    ((1, 2 ** 62, 4, 8, 2 ** 21, 8, 4, 4), INVALID),      # A extent overflows
+])
+def test_leading_dimension_checks(args, status):
+    assert ex(*args) == status
+
+
+@pytest.mark.parametrize("args", [
+    (1, 4, 4, 8, (8, 8, 4, 4), (0, 0, 0, 0)),             # packed
+    (1, 4, 4, 8, (16, 9, 4, 7), (0, 0, 0, 0)),            # padded rows
+    (2, 4, 4, 8, (8, 8, 4, 10), (32, 32, 16, 34)),        # D batches touch
+    (3, 4, 4, 8, (8, 8, 4, 4), (0, 0, 16, 16)),           # A, B broadcast
+])
+def test_leading_dimensions_accepted(args):
+    batch, M, N, K, lds, strides = args
+    assert "error" not in g.describe(batch, M, N, K, lds=lds,
+                                     strides=strides)
+
+
+def test_leading_dimensions_choose_the_loaders():
+    # rows of A padded to a multiple of 8 elements: vector loader kept
+    p = describe(1, 512, 512, 512, lds=(520, 512, 512, 512))
+    assert p["loader"] == "direct"
+    # an odd row stride rules out 16-byte loads
+    assert describe(1, 512, 512, 512, lds=(513, 512, 512, 512))["loader"] \
+        == "elem"
+    # D rows of 516 fp16 (1032 bytes) are not 16-byte aligned: element stores
+    assert describe(1, 512, 512, 512, lds=(512, 512, 512, 516))["vec_out"] \
+        == "0"
+    assert describe(1, 512, 512, 512, lds=(512, 512, 512, 520))["vec_out"] \
+        == "1"
+
+
+def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True, lds=None):
+    d = g.describe(batch, M, N, K, beta, out, aligned, lds=lds)
     return dict(kv.split("=") for kv in d.split()) if "=" in d else d
 
 

@@ -298,3 +298,73 @@ def test_split_k_workspace_reuse(monkeypatch):
         ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
         res = oracle.check_exact(CD.cpu().numpy(), ref, out)
         assert res.ok, f"{batch}x{M}x{N}x{K}: {res}"
+
+
+def _padded(arr, ld, fill):
+    """A (batch, rows, cols) array copied into a (batch, rows, ld) buffer
+    whose padding columns hold `fill`."""
+    batch, rows, cols = arr.shape
+    buf = np.full((batch, rows, ld), fill, dtype=arr.dtype)
+    buf[:, :, :cols] = arr
+    return buf
+
+
+LD_CASES = [
+    # batch, M, N, K, out, beta, (pad_a, pad_b, pad_c, pad_d)
+    (2, 300, 260, 832, "f16", 0.0, (8, 16, 0, 24)),      # 16-byte rows kept
+    (2, 129, 200, 1000, "f32", -2.0, (8, 8, 4, 12)),
+    (1, 70, 90, 37, "f32", 0.5, (3, 1, 5, 7)),           # odd row strides
+    (3, 64, 66, 64, "f16", 0.0, (1, 8, 0, 2)),
+]
+
+
+@pytest.mark.parametrize("spec", CONFIGS)
+def test_leading_dimensions(spec, monkeypatch):
+    """gemm_tn_ex on row-strided sub-matrices: padding of A and B holds NaN
+    (a read of it would poison the sums), padding of D holds a sentinel
+    that must survive."""
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    for (batch, M, N, K, out, beta, pads) in LD_CASES:
+        w = _int_workload(batch, M, N, K, out, alpha=0.5, beta=beta)
+        lda, ldb, ldc, ldd = K + pads[0], K + pads[1], N + pads[2], N + pads[3]
+        dt = np.float16 if out == "f16" else np.float32
+        A = torch.from_numpy(_padded(w.A, lda, np.nan)).cuda()
+        B = torch.from_numpy(_padded(w.B, ldb, np.nan)).cuda()
+        C = (torch.from_numpy(_padded(w.C, ldc, np.nan)).cuda()
+             if w.C is not None else None)
+        D = torch.from_numpy(_padded(np.zeros((batch, M, N), dt), ldd,
+                                     dt(1234.0))).cuda()
+        _say(f"[ld] {spec} {batch}x{M}x{N}x{K} {out} lds={lda},{ldb},{ldc},{ldd}")
+        st = g.gemm_tn_ex(
+            batch, M, N, K, w.alpha, A.data_ptr(), lda, M * lda, B.data_ptr(),
+            ldb, N * ldb, w.beta, C.data_ptr() if C is not None else None, ldc,
+            M * ldc, D.data_ptr(), ldd, M * ldd,
+            g.GEMM_TN_F16 if out == "f16" else g.GEMM_TN_F32,
+            torch.cuda.current_stream().cuda_stream)
+        assert st == g.OK
+        d = D.cpu().numpy()
+        assert np.all(d[:, :, N:] == dt(1234.0)), "D padding was written"
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(np.ascontiguousarray(d[:, :, :N]), ref, out)
+        assert res.ok, f"{spec} {M}x{N}x{K} lds {lda},{ldb},{ldc},{ldd}: {res}"
+
+
+def test_binding_takes_row_slices():
+    """The Python binding passes a tensor's row stride through, so column
+    slices of wider arrays need no copy."""
+    g = _gpu()
+    w = _int_workload(1, 96, 80, 200, "f32", alpha=1.0, beta=1.0)
+    Abig = torch.full((96, 256), float("nan"), dtype=torch.float16,
+                      device="cuda")
+    Bbig = torch.full((80, 208), float("nan"), dtype=torch.float16,
+                      device="cuda")
+    Abig[:, :200] = torch.from_numpy(w.A[0]).cuda()
+    Bbig[:, :200] = torch.from_numpy(w.B[0]).cuda()
+    Dbig = torch.full((96, 100), 7.0, device="cuda")
+    C = torch.from_numpy(w.C[0]).cuda()
+    g.gemm_tn(Abig[:, :200], Bbig[:, :200], 1.0, 1.0, C, out=Dbig[:, :80])
+    d = Dbig.cpu().numpy()
+    assert np.all(d[:, 80:] == 7.0)
+    ref = oracle.gemm_tn(w.A[0], w.B[0], 1.0, 1.0, w.C[0])
+    assert oracle.check_exact(np.ascontiguousarray(d[:, :80]), ref, "f32").ok

@@ -8,11 +8,12 @@ library is missing, importing the package raises ImportError.
     D = gemm_tn(A, B, alpha=1.0, beta=0.0, C=None, out_dtype=torch.float16)
 
 A: (M, K) or (batch, M, K) float16, B: (N, K) or (batch, N, K) float16,
-C / D: (M, N) or (batch, M, N) of out_dtype, all on the GPU.  Each matrix
-must be row-major with unit element stride; its row stride (leading
-dimension) and batch stride are taken from the tensor, so row slices of a
-wider array (and, for A and B, a batch dimension made by expand) are
-accepted without a copy.
+C / D: (M, N) or (batch, M, N) of out_dtype, all on the GPU.  Row and
+batch strides are taken from the tensors, so slices of wider arrays (and,
+for A and B, a batch dimension made by expand) need no copy.  C and D must
+have unit stride along N.  A and B may have unit stride along K (the TN
+layout) or along M / N: a transposed view such as `At.t()` of a
+contiguous (K, M) tensor is passed as an operand stored along M.
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libgemm_tn.so")
 
 GEMM_TN_F16, GEMM_TN_F32 = 0, 1
+GEMM_TN_ROW_K, GEMM_TN_ROW_MN = 0, 1
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(5)
 
 # torch bundles its own HIP runtime under the same soname as the system one
@@ -54,13 +56,13 @@ _lib.gemm_tn_strided_batched.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp,
                                          _i64, _vp, _i64, _f32, _vp, _i64,
                                          _vp, _i64, _int, _vp]
 _lib.gemm_tn_ex.restype = _int
-_lib.gemm_tn_ex.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp, _i64, _i64,
-                            _vp, _i64, _i64, _f32, _vp, _i64, _i64, _vp, _i64,
-                            _i64, _int, _vp]
+_lib.gemm_tn_ex.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp, _int, _i64,
+                            _i64, _vp, _int, _i64, _i64, _f32, _vp, _i64, _i64,
+                            _vp, _i64, _i64, _int, _vp]
 _lib.gemm_tn_describe.restype = _int
-_lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _i64, _i64, _i64,
-                                  _i64, _i64, _i64, _i64, _i64, _f32, _int,
-                                  _int, ctypes.c_char_p, _i64]
+_lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _int, _i64, _int,
+                                  _i64, _i64, _i64, _i64, _i64, _i64, _i64,
+                                  _f32, _int, _int, ctypes.c_char_p, _i64]
 _lib.gemm_tn_status_string.restype = ctypes.c_char_p
 _lib.gemm_tn_status_string.argtypes = [_int]
 _lib.gemm_tn_version.restype = _int
@@ -90,15 +92,20 @@ def lib() -> ctypes.CDLL:
 
 
 def describe(batch, M, N, K, beta=0.0, out_dtype="f16", aligned16=True,
-             strides=None, lds=None) -> str:
+             strides=None, lds=None, layouts=(GEMM_TN_ROW_K, GEMM_TN_ROW_K)
+             ) -> str:
     """Kernel configuration the library picks for this problem.
-    lds = (lda, ldb, ldc, ldd), packed rows by default."""
+    lds = (lda, ldb, ldc, ldd), packed rows by default; layouts =
+    (layout_a, layout_b)."""
+    la, lb = layouts
     if lds is None:
-        lds = (K, K, N, N)
+        lds = (M if la else K, N if lb else K, N, N)
     if strides is None:
-        strides = (M * lds[0], N * lds[1], M * lds[2], M * lds[3])
+        strides = ((K if la else M) * lds[0], (K if lb else N) * lds[1],
+                   M * lds[2], M * lds[3])
     buf = ctypes.create_string_buffer(256)
-    _lib.gemm_tn_describe(batch, M, N, K, *lds, *strides, float(beta),
+    _lib.gemm_tn_describe(batch, M, N, K, la, lds[0], lb, lds[1], lds[2],
+                          lds[3], *strides, float(beta),
                           GEMM_TN_F16 if out_dtype == "f16" else GEMM_TN_F32,
                           1 if aligned16 else 0, buf, len(buf))
     return buf.value.decode()
@@ -124,11 +131,21 @@ def _stream_handle(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _check_operand(t, name):
+def _operand(t, name):
+    """(layout, row stride) of a 2-D operand or of each matrix of a batch:
+    unit stride along K, else unit stride along M / N."""
     torch = _torch()
     if t.dtype != torch.float16:
         raise TypeError(f"{name} must be float16")
-    _check_layout(t, name)
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    rows, k = t.shape[-2], t.shape[-1]
+    if k <= 1 or t.stride(-1) == 1:
+        return GEMM_TN_ROW_K, _ld(t)
+    if rows <= 1 or t.stride(-2) == 1:
+        return GEMM_TN_ROW_MN, t.stride(-1) if k > 1 else max(rows, 1)
+    raise ValueError(f"{name} needs unit stride along its last or "
+                     "second-to-last dimension")
 
 
 def _check_layout(t, name):
@@ -154,8 +171,8 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
     `out` may be given (it is then D and is returned); otherwise D is
     allocated with `out_dtype` (default: C's dtype, else float16)."""
     torch = _torch()
-    _check_operand(A, "A")
-    _check_operand(B, "B")
+    layout_a, lda = _operand(A, "A")
+    layout_b, ldb = _operand(B, "B")
     if A.dim() != B.dim() or A.dim() not in (2, 3):
         raise ValueError("A and B must both be 2-D or both 3-D")
     batched = A.dim() == 3
@@ -188,9 +205,10 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
         _check_layout(C, "C")
         c_ptr, ldc, sc = C.data_ptr(), _ld(C), _bstride(C)
     st = _lib.gemm_tn_ex(
-        batch, M, N, K, float(alpha), A.data_ptr(), _ld(A), _bstride(A),
-        B.data_ptr(), _ld(B), _bstride(B), float(beta), c_ptr, ldc, sc,
-        out.data_ptr(), _ld(out), _bstride(out), code, _stream_handle(stream))
+        batch, M, N, K, float(alpha), A.data_ptr(), layout_a, lda,
+        _bstride(A), B.data_ptr(), layout_b, ldb, _bstride(B), float(beta),
+        c_ptr, ldc, sc, out.data_ptr(), _ld(out), _bstride(out), code,
+        _stream_handle(stream))
     if st != OK:
         raise GemmError(st)
     return out
@@ -215,9 +233,10 @@ def gemm_tn_raw(M, N, K, alpha, A_ptr, B_ptr, beta, C_ptr, D_ptr, d_dtype,
 
 def gemm_tn_ex(batch, M, N, K, alpha, A_ptr, lda, strideA, B_ptr, ldb,
                strideB, beta, C_ptr, ldc, strideC, D_ptr, ldd, strideD,
-               d_dtype, stream_handle) -> int:
+               d_dtype, stream_handle, layout_a=GEMM_TN_ROW_K,
+               layout_b=GEMM_TN_ROW_K) -> int:
     """Raw-pointer call of gemm_tn_ex(); returns the status code."""
-    return _lib.gemm_tn_ex(batch, M, N, K, float(alpha), A_ptr, lda, strideA,
-                           B_ptr, ldb, strideB, float(beta), C_ptr, ldc,
-                           strideC, D_ptr, ldd, strideD, d_dtype,
-                           stream_handle)
+    return _lib.gemm_tn_ex(batch, M, N, K, float(alpha), A_ptr, layout_a, lda,
+                           strideA, B_ptr, layout_b, ldb, strideB,
+                           float(beta), C_ptr, ldc, strideC, D_ptr, ldd,
+                           strideD, d_dtype, stream_handle)

@@ -92,12 +92,21 @@ bool vector_outputs(bool d_aligned16, bool c_aligned16, int64_t N,
             (c_aligned16 && (ld.c * es) % 16 == 0 && (sC * es) % 16 == 0));
 }
 
-int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
-        const void *A, int64_t lda, int64_t sA, const void *B, int64_t ldb,
-        int64_t sB, float beta, const void *C, int64_t ldc, int64_t sC,
-        void *D, int64_t ldd, int64_t sD, int d_dtype, void *stream)
+bool layout_ok(int layout)
 {
-    const Lds ld{lda, ldb, ldc, ldd};
+    return layout == GEMM_TN_ROW_K || layout == GEMM_TN_ROW_MN;
+}
+
+int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
+        const void *A, int layout_a, int64_t lda, int64_t sA, const void *B,
+        int layout_b, int64_t ldb, int64_t sB, float beta, const void *C,
+        int64_t ldc, int64_t sC, void *D, int64_t ldd, int64_t sD,
+        int d_dtype, void *stream)
+{
+    if (!layout_ok(layout_a) || !layout_ok(layout_b))
+        return GEMM_TN_ERR_INVALID_ARG;
+    const Lds ld{lda, ldb, ldc, ldd, layout_a == GEMM_TN_ROW_MN,
+                 layout_b == GEMM_TN_ROW_MN};
     int st = check_sizes(batch, M, N, K, ld, sA, sB, sC, sD, d_dtype);
     if (st != GEMM_TN_OK)
         return st;
@@ -132,6 +141,8 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.ldb = ldb;
     a.ldc = ldc;
     a.ldd = ldd;
+    a.a_mn = ld.a_mn;
+    a.b_mn = ld.b_mn;
     a.sA = sA;
     a.sB = sB;
     a.sC = sC;
@@ -180,8 +191,9 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
             const void *B, float beta, const void *C, void *D, int d_dtype,
             void *stream)
 {
-    return gtn::run(1, M, N, K, alpha, A, K, 0, B, K, 0, beta, C, N, 0, D, N,
-                    0, d_dtype, stream);
+    return gtn::run(1, M, N, K, alpha, A, GEMM_TN_ROW_K, K, 0, B,
+                    GEMM_TN_ROW_K, K, 0, beta, C, N, 0, D, N, 0, d_dtype,
+                    stream);
 }
 
 int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -190,27 +202,37 @@ int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
                             const void *C, int64_t strideC, void *D,
                             int64_t strideD, int d_dtype, void *stream)
 {
-    return gtn::run(batch, M, N, K, alpha, A, K, strideA, B, K, strideB, beta,
-                    C, N, strideC, D, N, strideD, d_dtype, stream);
+    return gtn::run(batch, M, N, K, alpha, A, GEMM_TN_ROW_K, K, strideA, B,
+                    GEMM_TN_ROW_K, K, strideB, beta, C, N, strideC, D, N,
+                    strideD, d_dtype, stream);
 }
 
 int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
-               const void *A, int64_t lda, int64_t strideA, const void *B,
-               int64_t ldb, int64_t strideB, float beta, const void *C,
-               int64_t ldc, int64_t strideC, void *D, int64_t ldd,
-               int64_t strideD, int d_dtype, void *stream)
+               const void *A, int layout_a, int64_t lda, int64_t strideA,
+               const void *B, int layout_b, int64_t ldb, int64_t strideB,
+               float beta, const void *C, int64_t ldc, int64_t strideC,
+               void *D, int64_t ldd, int64_t strideD, int d_dtype,
+               void *stream)
 {
-    return gtn::run(batch, M, N, K, alpha, A, lda, strideA, B, ldb, strideB,
-                    beta, C, ldc, strideC, D, ldd, strideD, d_dtype, stream);
+    return gtn::run(batch, M, N, K, alpha, A, layout_a, lda, strideA, B,
+                    layout_b, ldb, strideB, beta, C, ldc, strideC, D, ldd,
+                    strideD, d_dtype, stream);
 }
 
 int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
-                     int64_t lda, int64_t ldb, int64_t ldc, int64_t ldd,
-                     int64_t strideA, int64_t strideB, int64_t strideC,
-                     int64_t strideD, float beta, int d_dtype, int aligned16,
-                     char *buf, int64_t buflen)
+                     int layout_a, int64_t lda, int layout_b, int64_t ldb,
+                     int64_t ldc, int64_t ldd, int64_t strideA,
+                     int64_t strideB, int64_t strideC, int64_t strideD,
+                     float beta, int d_dtype, int aligned16, char *buf,
+                     int64_t buflen)
 {
-    const gtn::Lds ld{lda, ldb, ldc, ldd};
+    if (!gtn::layout_ok(layout_a) || !gtn::layout_ok(layout_b)) {
+        gtn::Plan bad;
+        bad.status = GEMM_TN_ERR_INVALID_ARG;
+        return gtn::describe_plan(bad, buf, buflen);
+    }
+    const gtn::Lds ld{lda, ldb, ldc, ldd, layout_a == GEMM_TN_ROW_MN,
+                      layout_b == GEMM_TN_ROW_MN};
     const int es = d_dtype == GEMM_TN_F32 ? 4 : 2;
     const bool vec_in =
         gtn::vector_inputs(aligned16 != 0, K, ld, strideA, strideB);

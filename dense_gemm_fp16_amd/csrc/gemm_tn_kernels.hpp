@@ -73,6 +73,7 @@ struct GemmArgs {
     float *ws;          // split-K partials: [split][batch][M][ws_ld] fp32
     int64_t M, N, K;
     int64_t lda, ldb, ldc, ldd;   // row strides in elements
+    int a_mn, b_mn;     // operand stored K x M (K x N) row-major instead
     int64_t sA, sB, sC, sD;       // batch strides in elements
     int64_t ws_ld;
     float alpha, beta;
@@ -424,13 +425,31 @@ gemm_tn_kernel(GemmArgs p)
     static_assert(BM % RB == 0, "slot blocks do not straddle A and B");
     u32x4 stage_regs[LOADER == LOAD_DIRECT ? 1 : SLOTS];
 
+    // An operand stored contiguous along M (N), i.e. element (row, k) at
+    // [k * ld + row] (the element loader only): its resource starts at row
+    // k0 of the stored matrix, column m0 (n0), so offsets stay within 32
+    // bits, and ends with row k_end - 1; rows past K and columns past M (N)
+    // read as zero.
+    auto mn_rsrc = [&](const _Float16 *X, int64_t sX, int64_t ld, int64_t c0,
+                       int64_t cols, int64_t k0) {
+        const int64_t rows = k_end - k0;
+        return make_rsrc(X + tc.b * sX + k0 * ld + c0,
+                         rows > 0 ? ((rows - 1) * ld + cols - c0) * 2 : 0);
+    };
     auto fetch_regs = [&](int64_t k0) {
+        __amdgpu_buffer_rsrc_t rAk = rA, rBk = rB;
+        if (LOADER == LOAD_ELEM) {
+            if (p.a_mn)
+                rAk = mn_rsrc(p.A, p.sA, lda, m0, M, k0);
+            if (p.b_mn)
+                rBk = mn_rsrc(p.B, p.sB, ldb, n0, N, k0);
+        }
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const bool isA = i * RB < BM;
             const int row = (isA ? i * RB : i * RB - BM) + tid / CHUNKS;
             const int lch = tid % CHUNKS;
-            const __amdgpu_buffer_rsrc_t r = isA ? rA : rB;
+            const __amdgpu_buffer_rsrc_t r = isA ? rAk : rBk;
             const int64_t ld = isA ? lda : ldb;
             const int64_t kk = k0 + lch * 8;
             if (LOADER == LOAD_VREG) {
@@ -440,12 +459,16 @@ gemm_tn_kernel(GemmArgs p)
                 stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off,
                                                                       0, 0);
             } else {
+                const bool mn = isA ? p.a_mn : p.b_mn;
+                const bool row_in = row < (isA ? M - m0 : N - n0);
                 uint16_t e[8];
 #pragma unroll
                 for (int x = 0; x < 8; ++x) {
                     const uint32_t off =
-                        kk + x < k_end ? (uint32_t)((row * ld + kk + x) * 2)
-                                       : kOutOfRange;
+                        kk + x >= k_end ? kOutOfRange
+                        : !mn           ? (uint32_t)((row * ld + kk + x) * 2)
+                        : row_in ? (uint32_t)(((kk - k0 + x) * ld + row) * 2)
+                                 : kOutOfRange;
                     e[x] = __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
                 }
                 stage_regs[i] = u32x4{e[0] | ((uint32_t)e[1] << 16),

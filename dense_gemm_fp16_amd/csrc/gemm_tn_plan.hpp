@@ -64,12 +64,13 @@ inline bool mul_ok(int64_t a, int64_t b, int64_t *out)
     return !__builtin_mul_overflow(a, b, out);
 }
 
-// Leading dimensions (row strides, in elements) of the four matrices.
+// Row strides (in elements) of the four matrices, and whether A (B) is
+// stored K x M (K x N) row-major -- contiguous along M (N) -- instead of
+// M x K (N x K).
 struct Lds {
     int64_t a, b, c, d;
+    bool a_mn = false, b_mn = false;
 };
-
-inline Lds packed_lds(int64_t N, int64_t K) { return Lds{K, K, N, N}; }
 
 // Size, stride and dtype checks (no pointers involved).  Every row stride
 // is at least its row length; batches of D may not overlap.
@@ -83,7 +84,10 @@ inline int check_sizes(int64_t batch, int64_t M, int64_t N, int64_t K,
         return GEMM_TN_ERR_INVALID_ARG;
     if (sA < 0 || sB < 0 || sC < 0 || sD < 0)
         return GEMM_TN_ERR_INVALID_ARG;
-    if (ld.a < K || ld.b < K || ld.c < N || ld.d < N)
+    // Stored rows and row lengths of A and B.
+    const int64_t a_rows = ld.a_mn ? K : M, a_len = ld.a_mn ? M : K;
+    const int64_t b_rows = ld.b_mn ? K : N, b_len = ld.b_mn ? N : K;
+    if (ld.a < a_len || ld.b < b_len || ld.c < N || ld.d < N)
         return GEMM_TN_ERR_INVALID_ARG;
     // Element extents of one matrix: (rows - 1) * ld + row length.
     int64_t ea, eb, ed, t;
@@ -94,8 +98,9 @@ inline int check_sizes(int64_t batch, int64_t M, int64_t N, int64_t K,
         }
         return mul_ok(rows - 1, l, out) && !__builtin_add_overflow(*out, len, out);
     };
-    if (!extent(M, ld.a, K, &ea) || !extent(N, ld.b, K, &eb) ||
-        !extent(M, ld.d, N, &ed) || !extent(M, ld.c, N, &t))
+    if (!extent(a_rows, ld.a, a_len, &ea) ||
+        !extent(b_rows, ld.b, b_len, &eb) || !extent(M, ld.d, N, &ed) ||
+        !extent(M, ld.c, N, &t))
         return GEMM_TN_ERR_INVALID_ARG;
     if (ea > t)
         t = ea;
@@ -233,6 +238,9 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (p.splits == 1)
         p.k_split = cdiv(K, kBK) * kBK;
 
+    // Operands contiguous along M or N go through the element loader.
+    if (ld.a_mn || ld.b_mn)
+        vec_in = false;
     p.loader = vec_in ? kDefaultVecLoader : PLAN_LOAD_ELEM;
     if (o.loader >= 0 && (vec_in || o.loader == PLAN_LOAD_ELEM))
         p.loader = o.loader;

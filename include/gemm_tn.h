@@ -22,10 +22,12 @@
  *   - K == 0 gives D = beta*C (an empty sum); M == 0 or N == 0 is a no-op.
  *
  * Layout: every matrix is row-major.  gemm_tn and gemm_tn_strided_batched
- * take packed rows (lda = ldb = K, ldc = ldd = N); gemm_tn_ex takes any row
- * strides, as gemm_device takes a stride per matrix (page "gemm_device
- * line-by-line walk-through", section 1: the global tensors are built from
- * a pointer, a shape and the strides dA, dB, dC).
+ * take A as M x K and B as N x K with packed rows (lda = ldb = K,
+ * ldc = ldd = N); gemm_tn_ex takes any row strides, and A or B may instead
+ * be stored transposed (K x M, K x N), as gemm_device takes a stride per
+ * matrix (page "gemm_device line-by-line walk-through", section 1: the
+ * global tensors are built from a pointer, a shape and the strides dA, dB,
+ * dC, so either mode of A and B may be the contiguous one).
  * Element types: A and B are IEEE binary16; C and D share `d_dtype`.
  *
  * Ownership and asynchrony: the caller owns every buffer; they are device
@@ -60,6 +62,14 @@ typedef enum gemm_tn_dtype {
     GEMM_TN_F32 = 1  /* IEEE binary32 */
 } gemm_tn_dtype;
 
+/* Storage of an operand (gemm_tn_ex). */
+typedef enum gemm_tn_layout {
+    GEMM_TN_ROW_K = 0,  /* contiguous along K: A(m,k) = A[m*lda + k],
+                           B(n,k) = B[n*ldb + k] (the TN layout) */
+    GEMM_TN_ROW_MN = 1  /* contiguous along M / N: A(m,k) = A[k*lda + m],
+                           B(n,k) = B[k*ldb + n] */
+} gemm_tn_layout;
+
 typedef enum gemm_tn_status {
     GEMM_TN_OK = 0,
     GEMM_TN_ERR_INVALID_ARG = 1, /* negative size, NULL where data is needed,
@@ -67,9 +77,10 @@ typedef enum gemm_tn_status {
                                     row, overlapping batches of D, size
                                     overflow */
     GEMM_TN_ERR_UNSUPPORTED = 2, /* sizes beyond the kernels' addressing
-                                    range: K or an A/B row stride > 2^21,
-                                    N or a C/D row stride > 2^20, or
-                                    M > 2^31 - 1 */
+                                    range: K or an A/B row stride > 2^21
+                                    (so M or N > 2^21 for an operand stored
+                                    along M / N), N or a C/D row stride >
+                                    2^20, or M > 2^31 - 1 */
     GEMM_TN_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
     GEMM_TN_ERR_WORKSPACE = 4    /* the split-K workspace could not be
                                     allocated */
@@ -112,23 +123,28 @@ int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
 /*
  * The general form: gemm_tn_strided_batched with a row stride (leading
  * dimension, in elements) per matrix, so that any row-major sub-matrix of
- * a larger array can be an operand or the output:
- *   A(m,k) = A[i*strideA + m*lda + k],   lda >= K
- *   B(n,k) = B[i*strideB + n*ldb + k],   ldb >= K
+ * a larger array can be an operand or the output, and with the storage of
+ * A and B chosen by layout_a / layout_b (gemm_tn_layout):
+ *   A(m,k) = A[i*strideA + m*lda + k],   lda >= K   (GEMM_TN_ROW_K)
+ *            A[i*strideA + k*lda + m],   lda >= M   (GEMM_TN_ROW_MN)
+ *   B(n,k) = B[i*strideB + n*ldb + k],   ldb >= K   (GEMM_TN_ROW_K)
+ *            B[i*strideB + k*ldb + n],   ldb >= N   (GEMM_TN_ROW_MN)
  *   C(m,n) = C[i*strideC + m*ldc + n],   ldc >= N
  *   D(m,n) = D[i*strideD + m*ldd + n],   ldd >= N
  * Only the M x N elements of each D are written; the ldd - N elements
- * between rows are left untouched.  Batches of D must not overlap:
- * strideD >= (M - 1)*ldd + N when batch > 1.  The 16-byte loaders need
- * lda and ldb to be multiples of 8 as well (otherwise the element loader
- * runs); 16-byte stores need ldd (and ldc when C is read) to keep rows on
- * 16-byte boundaries.
+ * between rows are left untouched, and no padding of A, B or C is read.
+ * Batches of D must not overlap: strideD >= (M - 1)*ldd + N when
+ * batch > 1.  The 16-byte loaders need K-contiguous operands with lda and
+ * ldb multiples of 8 (otherwise the element loader runs); 16-byte stores
+ * need ldd (and ldc when C is read) to keep rows on 16-byte boundaries.
+ * An unknown layout value is GEMM_TN_ERR_INVALID_ARG.
  */
 int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
-               const void *A, int64_t lda, int64_t strideA, const void *B,
-               int64_t ldb, int64_t strideB, float beta, const void *C,
-               int64_t ldc, int64_t strideC, void *D, int64_t ldd,
-               int64_t strideD, int d_dtype, void *stream);
+               const void *A, int layout_a, int64_t lda, int64_t strideA,
+               const void *B, int layout_b, int64_t ldb, int64_t strideB,
+               float beta, const void *C, int64_t ldc, int64_t strideC,
+               void *D, int64_t ldd, int64_t strideD, int d_dtype,
+               void *stream);
 
 /*
  * Name of the kernel configuration gemm_tn_ex would launch for this
@@ -138,10 +154,11 @@ int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
  * GEMM_TN_OK or the status the GEMM call would return for these sizes.
  */
 int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
-                     int64_t lda, int64_t ldb, int64_t ldc, int64_t ldd,
-                     int64_t strideA, int64_t strideB, int64_t strideC,
-                     int64_t strideD, float beta, int d_dtype,
-                     int aligned16, char *buf, int64_t buflen);
+                     int layout_a, int64_t lda, int layout_b, int64_t ldb,
+                     int64_t ldc, int64_t ldd, int64_t strideA,
+                     int64_t strideB, int64_t strideC, int64_t strideD,
+                     float beta, int d_dtype, int aligned16, char *buf,
+                     int64_t buflen);
 
 /* Human-readable text of a status code (static storage). */
 const char *gemm_tn_status_string(int status);

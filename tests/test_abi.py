@@ -118,6 +118,37 @@ def test_leading_dimensions_accepted(args):
                                      strides=strides)
 
 
+def ex_layout(layout_a, layout_b, M, N, K, lda, ldb):
+    return g.gemm_tn_ex(1, M, N, K, 1.0, P, lda, 0, P, ldb, 0, 0.0, NULL, N,
+                        0, P, N, 0, F32, S, layout_a, layout_b)
+
+
+ROW_K, ROW_MN = g.GEMM_TN_ROW_K, g.GEMM_TN_ROW_MN
+
+
+@pytest.mark.parametrize("args,status", [
+    ((2, ROW_K, 4, 6, 8, 8, 8), INVALID),        # unknown layout value
+    ((ROW_K, -1, 4, 6, 8, 8, 8), INVALID),
+    ((ROW_MN, ROW_K, 4, 6, 8, 3, 8), INVALID),   # A stored K x M: lda >= M
+    ((ROW_K, ROW_MN, 4, 6, 8, 8, 5), INVALID),   # B stored K x N: ldb >= N
+    ((ROW_MN, ROW_K, 2 ** 21 + 8, 6, 8, 2 ** 21 + 8, 8), UNSUPPORTED),
+])
+def test_layout_checks(args, status):
+    assert ex_layout(*args) == status
+
+
+@pytest.mark.parametrize("la,lb", [(ROW_K, ROW_MN), (ROW_MN, ROW_K),
+                                   (ROW_MN, ROW_MN)])
+def test_operands_stored_along_m_or_n_are_planned(la, lb):
+    # lda >= M for A stored K x M (here M = 300 > K = 64 is fine)
+    p = describe(1, 300, 200, 64, layouts=(la, lb))
+    assert p["loader"] == "elem"      # element loader for these layouts
+    # a row stride that only covers K is too short for a row of M / N
+    short = (64, 64, 200, 200)
+    assert g.describe(1, 300, 200, 64, layouts=(la, lb), lds=short) \
+        == "error:1"
+
+
 def test_leading_dimensions_choose_the_loaders():
     # rows of A padded to a multiple of 8 elements: vector loader kept
     p = describe(1, 512, 512, 512, lds=(520, 512, 512, 512))
@@ -132,8 +163,10 @@ def test_leading_dimensions_choose_the_loaders():
         == "1"
 
 
-def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True, lds=None):
-    d = g.describe(batch, M, N, K, beta, out, aligned, lds=lds)
+def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True, lds=None,
+             layouts=(0, 0)):
+    d = g.describe(batch, M, N, K, beta, out, aligned, lds=lds,
+                   layouts=layouts)
     return dict(kv.split("=") for kv in d.split()) if "=" in d else d
 
 

@@ -368,3 +368,63 @@ def test_binding_takes_row_slices():
     assert np.all(d[:, 80:] == 7.0)
     ref = oracle.gemm_tn(w.A[0], w.B[0], 1.0, 1.0, w.C[0])
     assert oracle.check_exact(np.ascontiguousarray(d[:, :80]), ref, "f32").ok
+
+
+LAYOUT_CASES = [
+    # batch, M, N, K, out, beta, row-stride padding of the stored A and B
+    (2, 300, 260, 832, "f16", 0.0, (8, 3)),
+    (1, 129, 200, 1000, "f32", -2.0, (0, 0)),
+    (3, 70, 90, 37, "f32", 0.5, (5, 1)),
+]
+
+
+@pytest.mark.parametrize("layouts", [(0, 1), (1, 0), (1, 1)])
+@pytest.mark.parametrize("spec", ["tile=256,split=1", "tile=128,split=3",
+                                  "tile=64,split=1", "tile=64,split=3"])
+def test_operands_stored_along_m_or_n(layouts, spec, monkeypatch):
+    """A stored K x M and/or B stored K x N (gemm_tn_ex layouts), with
+    padded row strides whose padding holds NaN."""
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    la, lb = layouts
+    for (batch, M, N, K, out, beta, pads) in LAYOUT_CASES:
+        w = _int_workload(batch, M, N, K, out, alpha=0.5, beta=beta)
+        # stored matrices: rows x row length, then padded
+        As = np.ascontiguousarray(w.A.transpose(0, 2, 1)) if la else w.A
+        Bs = np.ascontiguousarray(w.B.transpose(0, 2, 1)) if lb else w.B
+        lda = As.shape[2] + pads[0]
+        ldb = Bs.shape[2] + pads[1]
+        A = torch.from_numpy(_padded(As, lda, np.nan)).cuda()
+        B = torch.from_numpy(_padded(Bs, ldb, np.nan)).cuda()
+        dt = np.float16 if out == "f16" else np.float32
+        C = torch.from_numpy(w.C).cuda() if w.C is not None else None
+        D = torch.empty((batch, M, N), dtype=torch.float16 if out == "f16"
+                        else torch.float32, device="cuda")
+        _say(f"[layout] {layouts} {spec} {batch}x{M}x{N}x{K} {out}")
+        st = g.gemm_tn_ex(
+            batch, M, N, K, w.alpha, A.data_ptr(), lda, As.shape[1] * lda,
+            B.data_ptr(), ldb, Bs.shape[1] * ldb, w.beta,
+            C.data_ptr() if C is not None else None, N, M * N, D.data_ptr(),
+            N, M * N, g.GEMM_TN_F16 if out == "f16" else g.GEMM_TN_F32,
+            torch.cuda.current_stream().cuda_stream, la, lb)
+        assert st == g.OK
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(D.cpu().numpy().astype(dt), ref, out)
+        assert res.ok, f"{layouts} {spec} {M}x{N}x{K}: {res}"
+
+
+def test_binding_takes_transposed_views():
+    """A transposed view (unit stride along M or N) is passed as an operand
+    stored along M / N, without a copy."""
+    g = _gpu()
+    w = _int_workload(2, 96, 80, 200, "f32")
+    At = torch.from_numpy(np.ascontiguousarray(
+        w.A.transpose(0, 2, 1))).cuda()          # (batch, K, M)
+    Bt = torch.from_numpy(np.ascontiguousarray(
+        w.B.transpose(0, 2, 1))).cuda()          # (batch, K, N)
+    ref = oracle.gemm_tn(w.A, w.B)
+    for A, B in [(At.transpose(1, 2), torch.from_numpy(w.B).cuda()),
+                 (torch.from_numpy(w.A).cuda(), Bt.transpose(1, 2)),
+                 (At.transpose(1, 2), Bt.transpose(1, 2))]:
+        D = g.gemm_tn(A, B, out_dtype=torch.float32)
+        assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok

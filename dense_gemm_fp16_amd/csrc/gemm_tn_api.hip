@@ -76,11 +76,12 @@ bool aligned(const void *p, uintptr_t a)
 
 // vec_in: 16-byte loads of A and B are possible; vec_out: 16-byte stores
 // of D (and loads of C) are.
-bool vector_inputs(bool aligned16, int64_t K, const Lds &ld, int64_t sA,
-                   int64_t sB)
+bool vector_inputs(bool aligned16, int64_t M, int64_t N, int64_t K,
+                   const Lds &ld, int64_t sA, int64_t sB)
 {
-    return aligned16 && K % 8 == 0 && ld.a % 8 == 0 && ld.b % 8 == 0 &&
-           sA % 8 == 0 && sB % 8 == 0;
+    const int64_t a_len = ld.a_mn ? M : K, b_len = ld.b_mn ? N : K;
+    return aligned16 && a_len % 8 == 0 && b_len % 8 == 0 && ld.a % 8 == 0 &&
+           ld.b % 8 == 0 && sA % 8 == 0 && sB % 8 == 0;
 }
 
 bool vector_outputs(bool d_aligned16, bool c_aligned16, int64_t N,
@@ -118,8 +119,8 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
 
     const bool out_f32 = d_dtype == GEMM_TN_F32;
     const int es = out_f32 ? 4 : 2;
-    const bool vec_in =
-        vector_inputs(aligned(A, 16) && aligned(B, 16), K, ld, sA, sB);
+    const bool vec_in = vector_inputs(aligned(A, 16) && aligned(B, 16), M, N,
+                                      K, ld, sA, sB);
     const bool vec_out = vector_outputs(aligned(D, 16), aligned(C, 16), N, ld,
                                         sC, sD, beta, es);
     const Plan p = make_plan(batch, M, N, K, ld, sA, sB, sC, sD, d_dtype,
@@ -141,8 +142,6 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.ldb = ldb;
     a.ldc = ldc;
     a.ldd = ldd;
-    a.a_mn = ld.a_mn;
-    a.b_mn = ld.b_mn;
     a.sA = sA;
     a.sB = sB;
     a.sC = sC;
@@ -165,15 +164,15 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     hipError_t e;
     switch (p.tile) {
     case TILE_256:
-        e = launch_tile256(a, p.loader, out_f32, split, p.vec_out,
+        e = launch_tile256(a, p.loader, p.layout, out_f32, split, p.vec_out,
                            (unsigned)p.grid, s);
         break;
     case TILE_128:
-        e = launch_tile128(a, p.loader, out_f32, split, p.vec_out,
+        e = launch_tile128(a, p.loader, p.layout, out_f32, split, p.vec_out,
                            (unsigned)p.grid, s);
         break;
     default:
-        e = launch_tile64(a, p.loader, out_f32, split, p.vec_out,
+        e = launch_tile64(a, p.loader, p.layout, out_f32, split, p.vec_out,
                           (unsigned)p.grid, s);
         break;
     }
@@ -234,8 +233,8 @@ int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
     const gtn::Lds ld{lda, ldb, ldc, ldd, layout_a == GEMM_TN_ROW_MN,
                       layout_b == GEMM_TN_ROW_MN};
     const int es = d_dtype == GEMM_TN_F32 ? 4 : 2;
-    const bool vec_in =
-        gtn::vector_inputs(aligned16 != 0, K, ld, strideA, strideB);
+    const bool vec_in = gtn::vector_inputs(aligned16 != 0, M, N, K, ld,
+                                           strideA, strideB);
     const bool vec_out = gtn::vector_outputs(aligned16 != 0, aligned16 != 0,
                                              N, ld, strideC, strideD, beta, es);
     const gtn::Plan p = gtn::make_plan(batch, M, N, K, ld, strideA, strideB,

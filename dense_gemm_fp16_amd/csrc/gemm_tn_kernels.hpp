@@ -50,6 +50,7 @@ namespace gtn {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -73,7 +74,6 @@ struct GemmArgs {
     float *ws;          // split-K partials: [split][batch][M][ws_ld] fp32
     int64_t M, N, K;
     int64_t lda, ldb, ldc, ldd;   // row strides in elements
-    int a_mn, b_mn;     // operand stored K x M (K x N) row-major instead
     int64_t sA, sB, sC, sD;       // batch strides in elements
     int64_t ws_ld;
     float alpha, beta;
@@ -140,9 +140,31 @@ __device__ __host__ constexpr int swizzle_chunk(int row, int chunk)
     return chunk ^ ((row / (128 / BK)) % (BK / 8));
 }
 
+// LDS swizzle of an operand tile stored along M (N): BK rows of k, each
+// CR = BM / 8 chunks of 16 bytes (8 consecutive m).  Its fragments are read
+// with ds_read_b64_tr_b16, where lane group g of a wave reads rows
+// 8g + 4r + (0..3) of a k-step, 32 bytes each; a half wave thus touches 8
+// rows {0..3, 8..11} (+4, +16, +32 ...) at one pair of chunks (c, c+1),
+// and XORing the chunk with 2*h(row) (h distinct over those 8 rows, and
+// kept below CR so the pair stays adjacent and in its 256-byte line) puts
+// them in distinct bank slots.  With 128-byte rows two rows share a
+// 256-byte line by parity, so h only has to separate rows of one parity.
+template <int CR>
+__device__ __host__ constexpr int swizzle_mn(int row, int chunk)
+{
+    static_assert(CR == 8 || CR % 16 == 0, "rows of 128 bytes or 256n");
+    return CR >= 16
+               ? chunk ^ (2 * ((row & 3) | (((row >> 3) & 1) << 2)))
+               : chunk ^ (2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1)));
+}
+
 template <bool V>
 struct Bool {
     static constexpr bool value = V;
+};
+template <int V>
+struct Int {
+    static constexpr int value = V;
 };
 
 // s_waitcnt with only the vector-memory counter (gfx9 encoding: vmcnt in
@@ -259,6 +281,10 @@ __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 //   MB : MFMA block edge, 32 (v_mfma_f32_32x32x16_f16) or 16
 //        (v_mfma_f32_16x16x32_f16: the same work per cycle, in four times as
 //        many instructions, at a lower power per flop on random data);
+//   LAY : bit 0 / bit 1 set = A / B is stored contiguous along M / N.
+//         The direct loader then loads its tile as k-rows and reads its
+//         fragments with ds_read_b64_tr_b16; the element loader gathers
+//         8 consecutive k of a row into the usual K-contiguous LDS tile;
 //   OutT : _Float16 or float; SPLIT : write fp32 partials to the workspace;
 //   VEC_OUT : rows of D (and C) start on 16-byte boundaries (N * element
 //             size a multiple of 16, D / C 16-byte aligned): the tile is
@@ -266,7 +292,7 @@ __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 // ---------------------------------------------------------------------------
 template <int BM, int BN, int BK, int WM, int WN, int STAGES, int LOADER,
           typename OutT, bool SPLIT, bool VEC_OUT, int MIN_WAVES, int SCHED,
-          int MB>
+          int MB, int LAY>
 __global__ void __attribute__((amdgpu_flat_work_group_size(WM * WN * 64,
                                                            WM * WN * 64),
                                amdgpu_waves_per_eu(MIN_WAVES, 8)))
@@ -292,6 +318,15 @@ gemm_tn_kernel(GemmArgs p)
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(WTM % MB == 0 && WTN % MB == 0, "wave tile of MFMA blocks");
     static_assert(BK % KM == 0, "whole k-steps per tile");
+    constexpr bool A_MN = (LAY & 1) != 0, B_MN = (LAY & 2) != 0;
+    // Tiles held in LDS as k-rows (direct loader); the element loader
+    // gathers operands stored along M / N into the K-contiguous tile.
+    constexpr bool A_TR = A_MN && LOADER == LOAD_DIRECT;
+    constexpr bool B_TR = B_MN && LOADER == LOAD_DIRECT;
+    static_assert(LAY == 0 || LOADER == LOAD_ELEM ||
+                      (LOADER == LOAD_DIRECT && MB == 16),
+                  "operands stored along M / N: element loader, or direct "
+                  "loader with 16x16 MFMA");
     static_assert(BM % (ROWS_PER_WAVE_LOAD * NW) == 0 &&
                       BN % (ROWS_PER_WAVE_LOAD * NW) == 0,
                   "every wave issues the same number of tile loads");
@@ -380,10 +415,64 @@ gemm_tn_kernel(GemmArgs p)
     // one per-lane chunk and offset; only a wave-uniform row stride differs.
     static_assert((NLOAD * ROWS_PER_WAVE_LOAD) % 16 == 0,
                   "a wave's row groups share the swizzle phase");
+    // An operand stored along M (N): the tile is BK rows of k, each BM (BN)
+    // elements; a 1 KiB load covers 1024 / (2*BM) rows.  Its resource
+    // starts at row k0, column m0 (n0) and ends with row k_end - 1, so
+    // offsets stay within 32 bits; rows past K and chunks past M (N, a
+    // multiple of 8 on this path) read as zero.
+    auto mn_rsrc = [&](const _Float16 *X, int64_t sX, int64_t ld, int64_t c0,
+                       int64_t cols, int64_t k0) {
+        const int64_t rows = k_end - k0;
+        return make_rsrc(X + tc.b * sX + k0 * ld + c0,
+                         rows > 0 ? ((rows - 1) * ld + cols - c0) * 2 : 0);
+    };
+    // Per-lane offsets of the loads of one wave into such a tile: the
+    // wave's load groups are RG k-rows apart, a multiple of 8, so the
+    // swizzle (a function of the row mod 16) takes at most two values, for
+    // even and odd groups; a group adds a wave-uniform row stride.
+    struct MnLanes {
+        uint32_t even, odd;   // offset of group 0 / group 1 minus the stride
+        int rk0;              // k-row of this lane in group 0
+        bool c_even, c_odd;   // the lane's chunk lies before M (N)
+    };
+    auto mn_lanes = [&](auto cr_tag, int lw, int64_t ld, int64_t cols_left) {
+        constexpr int CR = decltype(cr_tag)::value;
+        constexpr int RPL = 64 / CR;              // k-rows per 1 KiB load
+        constexpr int RG = NLOAD * RPL;
+        static_assert(RG % 8 == 0, "two swizzle phases per wave");
+        MnLanes m;
+        m.rk0 = lw * RPL + lane / CR;
+        const int ce = swizzle_mn<CR>(m.rk0, lane % CR);
+        const int co = swizzle_mn<CR>(m.rk0 + RG, lane % CR);
+        m.even = (uint32_t)((m.rk0 * ld + ce * 8) * 2);
+        m.odd = (uint32_t)((m.rk0 * ld + co * 8) * 2);
+        m.c_even = ce * 8 < cols_left;
+        m.c_odd = co * 8 < cols_left;
+        return m;
+    };
+    auto mn_offset = [&](auto cr_tag, const MnLanes &m, int g, int64_t k0,
+                         int64_t ld) {
+        constexpr int CR = decltype(cr_tag)::value;
+        constexpr int RG = NLOAD * (64 / CR);
+        const bool ok = (g & 1) ? m.c_odd : m.c_even;
+        return ok && k0 + m.rk0 + g * RG < k_end
+                   ? ((g & 1) ? m.odd : m.even) + (uint32_t)(g * RG * ld) * 2
+                   : kOutOfRange;
+    };
     auto issue_part = [&](int stage, int64_t k0, int lw, int x0, int x1) {
         GTN_LDS _Float16 *ldsp = (GTN_LDS _Float16 *)(lds);
         const int64_t rem64 = k_end - k0;
         const int rem = rem64 < 0 ? 0 : (rem64 > BK ? BK : (int)rem64);
+        __amdgpu_buffer_rsrc_t rAt = rA, rBt = rB;
+        MnLanes ma{}, mb{};
+        if constexpr (A_TR) {
+            rAt = mn_rsrc(p.A, p.sA, lda, m0, M, k0);
+            ma = mn_lanes(Int<BM / 8>{}, lw, lda, M - m0);
+        }
+        if constexpr (B_TR) {
+            rBt = mn_rsrc(p.B, p.sB, ldb, n0, N, k0);
+            mb = mn_lanes(Int<BN / 8>{}, lw, ldb, N - n0);
+        }
         const uint32_t kb = (uint32_t)(k0 < K ? k0 : K) * 2;
         const int row0 = lw * ROWS_PER_WAVE_LOAD + rrow;
         const int kc = swizzle_chunk<BK>(row0, pch) * 8;
@@ -400,12 +489,16 @@ gemm_tn_kernel(GemmArgs p)
                 continue;
             const bool isA = x < A_GROUPS;
             const int g = isA ? x : x - A_GROUPS;
-            const uint32_t off =
+            uint32_t off =
                 !valid ? kOutOfRange
                 : isA  ? lane_off_a + (uint32_t)g * group_stride_a
                        : lane_off_b + (uint32_t)g * group_stride_b;
+            if (isA && A_TR)
+                off = mn_offset(Int<BM / 8>{}, ma, g, k0, lda);
+            if (!isA && B_TR)
+                off = mn_offset(Int<BN / 8>{}, mb, g, k0, ldb);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                isA ? rA : rB,
+                isA ? rAt : rBt,
                 (GTN_LDS void *)(ldsp + (isA ? a_base(stage) : b_base(stage)) +
                                  (lw + g * NLOAD) * ROWS_PER_WAVE_LOAD * BK),
                 16, off, 0, 0, 0);
@@ -425,25 +518,14 @@ gemm_tn_kernel(GemmArgs p)
     static_assert(BM % RB == 0, "slot blocks do not straddle A and B");
     u32x4 stage_regs[LOADER == LOAD_DIRECT ? 1 : SLOTS];
 
-    // An operand stored contiguous along M (N), i.e. element (row, k) at
-    // [k * ld + row] (the element loader only): its resource starts at row
-    // k0 of the stored matrix, column m0 (n0), so offsets stay within 32
-    // bits, and ends with row k_end - 1; rows past K and columns past M (N)
-    // read as zero.
-    auto mn_rsrc = [&](const _Float16 *X, int64_t sX, int64_t ld, int64_t c0,
-                       int64_t cols, int64_t k0) {
-        const int64_t rows = k_end - k0;
-        return make_rsrc(X + tc.b * sX + k0 * ld + c0,
-                         rows > 0 ? ((rows - 1) * ld + cols - c0) * 2 : 0);
-    };
+    // The element loader reads an operand stored along M (N) through the
+    // same per-k-tile resource as the direct loader (mn_rsrc above).
     auto fetch_regs = [&](int64_t k0) {
         __amdgpu_buffer_rsrc_t rAk = rA, rBk = rB;
-        if (LOADER == LOAD_ELEM) {
-            if (p.a_mn)
-                rAk = mn_rsrc(p.A, p.sA, lda, m0, M, k0);
-            if (p.b_mn)
-                rBk = mn_rsrc(p.B, p.sB, ldb, n0, N, k0);
-        }
+        if constexpr (LOADER == LOAD_ELEM && A_MN)
+            rAk = mn_rsrc(p.A, p.sA, lda, m0, M, k0);
+        if constexpr (LOADER == LOAD_ELEM && B_MN)
+            rBk = mn_rsrc(p.B, p.sB, ldb, n0, N, k0);
 #pragma unroll
         for (int i = 0; i < SLOTS; ++i) {
             const bool isA = i * RB < BM;
@@ -459,7 +541,7 @@ gemm_tn_kernel(GemmArgs p)
                 stage_regs[i] = __builtin_amdgcn_raw_buffer_load_b128(r, off,
                                                                       0, 0);
             } else {
-                const bool mn = isA ? p.a_mn : p.b_mn;
+                const bool mn = isA ? A_MN : B_MN;
                 const bool row_in = row < (isA ? M - m0 : N - n0);
                 uint16_t e[8];
 #pragma unroll
@@ -493,6 +575,33 @@ gemm_tn_kernel(GemmArgs p)
     // ---- LDS -> registers, and the MFMAs of one KM-wide k-step ---------
     const int frow = lane % MB;
     const int fq = lane / MB;
+    // Fragment of an operand tile stored along M (N) (BK rows of W
+    // elements): rows c0 .. c0 + 15, the 32 k of k-step ks.  Each
+    // ds_read_b64_tr_b16 gives lane i of every 16-lane group the 4 values
+    // (k, c0 + i), k = kb .. kb + 3, when lane j of the group points at
+    // (kb + j / 4, c0 + 4 (j % 4)); lane group g takes k = 8g .. 8g + 7 of
+    // the k-step in two such reads.
+    auto read_tr = [&](auto w_tag, const _Float16 *s, int c0, int ks) {
+        constexpr int W = decltype(w_tag)::value;
+        constexpr int CR = W / 8;
+        const int i = lane & 15, g = lane >> 4;
+        const int col = c0 + 4 * (i & 3);
+        half8 out;
+#pragma unroll
+        for (int r = 0; r < 2; ++r) {
+            const int row = ks * 32 + 8 * g + 4 * r + (i >> 2);
+            const int pc = swizzle_mn<CR>(row, col >> 3);
+            const GTN_LDS _Float16 *a = (const GTN_LDS _Float16 *)s +
+                                        row * W + pc * 8 + (col & 7);
+            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (GTN_LDS s16x4 *)a);
+            const half4 h = __builtin_bit_cast(half4, v);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                out[4 * r + e] = h[e];
+        }
+        return out;
+    };
     // Fragments are read in the order the MFMAs below consume them (B0, A0,
     // then B1.., then A1..), so the first MFMAs of a k-step depend only on
     // the oldest reads of the previous one.
@@ -502,14 +611,22 @@ gemm_tn_kernel(GemmArgs p)
         const _Float16 *sB = lds + b_base(stb);
         const int ch = ks * QN + fq;
         auto rd_a = [&](int i) {
-            const int row = wm * WTM + i * MB + frow;
-            af[i] = *(const half8 *)(sA + row * BK +
-                                     swizzle_chunk<BK>(row, ch) * 8);
+            if constexpr (A_TR) {
+                af[i] = read_tr(Int<BM>{}, sA, wm * WTM + i * MB, ks);
+            } else {
+                const int row = wm * WTM + i * MB + frow;
+                af[i] = *(const half8 *)(sA + row * BK +
+                                         swizzle_chunk<BK>(row, ch) * 8);
+            }
         };
         auto rd_b = [&](int j) {
-            const int row = wn * WTN + j * MB + frow;
-            bf[j] = *(const half8 *)(sB + row * BK +
-                                     swizzle_chunk<BK>(row, ch) * 8);
+            if constexpr (B_TR) {
+                bf[j] = read_tr(Int<BN>{}, sB, wn * WTN + j * MB, ks);
+            } else {
+                const int row = wn * WTN + j * MB + frow;
+                bf[j] = *(const half8 *)(sB + row * BK +
+                                         swizzle_chunk<BK>(row, ch) * 8);
+            }
         };
         rd_b(0);
         rd_a(0);

@@ -27,6 +27,10 @@ constexpr int kTileWN[NUM_TILES] = {GTN_T256_WN, 2, 2};
 constexpr int kTileSched[NUM_TILES] = {GTN_T256_SCHED, 0, 0};
 constexpr int kTileMfma[NUM_TILES] = {GTN_T256_MFMA, GTN_T128_MFMA,
                                       GTN_T64_MFMA};
+constexpr int kTileDirectLays[NUM_TILES] = {
+    GTN_T256_DIRECT_LAYS, GTN_T128_DIRECT_LAYS, GTN_T64_DIRECT_LAYS};
+constexpr bool kTileElemLays[NUM_TILES] = {
+    GTN_T256_ELEM_LAYS, GTN_T128_ELEM_LAYS, GTN_T64_ELEM_LAYS};
 constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
@@ -47,6 +51,8 @@ struct Plan {
     int tile = TILE_64;
     int bm = 64, bn = 64;
     int loader = PLAN_LOAD_ELEM;
+    bool a_mn = false, b_mn = false;   // operand stored along M / N
+    int layout = 0;          // kernel layout bits (LAY of the kernel)
     bool vec_out = false;
     int splits = 1;
     int64_t k_split = 0;
@@ -180,8 +186,9 @@ inline Override parse_override(const char *s)
     return o;
 }
 
-// Choose the kernel configuration.  vec_in: A and B 16-byte aligned, K and
-// the A/B row and batch strides multiples of 8.  vec_out: every row of D
+// Choose the kernel configuration.  vec_in: A and B 16-byte aligned, their
+// row lengths (K, or M / N when stored along M / N) and row and batch
+// strides multiples of 8.  vec_out: every row of D
 // (and of C when it is read) starts on a 16-byte boundary and holds a
 // whole number of 16-byte chunks.
 inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -214,6 +221,30 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         tile = TILE_64;
     if (o.tile >= 0)
         tile = o.tile;
+    // Operands stored along M / N: the loader that will run (direct when
+    // the rows allow 16-byte loads) must have a kernel for this layout on
+    // the tile, else the next smaller tile is taken.
+    const int layout = (ld.a_mn ? 1 : 0) | (ld.b_mn ? 2 : 0);
+    int loader = vec_in ? kDefaultVecLoader : PLAN_LOAD_ELEM;
+    if (o.loader >= 0 && (vec_in || o.loader == PLAN_LOAD_ELEM))
+        loader = o.loader;
+    if (layout != 0 && loader == PLAN_LOAD_VREG)
+        loader = PLAN_LOAD_ELEM;
+    auto has_kernel = [&](int t) -> bool {
+        if (loader == PLAN_LOAD_DIRECT)
+            return ((kTileDirectLays[t] >> layout) & 1) != 0;
+        if (loader == PLAN_LOAD_ELEM)
+            return layout == 0 || kTileElemLays[t];
+        return layout == 0;
+    };
+    while (!has_kernel(tile) && tile + 1 < NUM_TILES)
+        ++tile;
+    if (!has_kernel(tile) && loader == PLAN_LOAD_DIRECT) {
+        loader = PLAN_LOAD_ELEM;     // no direct kernel for the layout
+        tile = o.tile >= 0 ? o.tile : tile;
+        while (!has_kernel(tile) && tile + 1 < NUM_TILES)
+            ++tile;
+    }
     p.tile = tile;
     p.bm = p.bn = kTileDim[tile];
     p.tiles_m = (int)cdiv(M, p.bm);
@@ -238,12 +269,10 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (p.splits == 1)
         p.k_split = cdiv(K, kBK) * kBK;
 
-    // Operands contiguous along M or N go through the element loader.
-    if (ld.a_mn || ld.b_mn)
-        vec_in = false;
-    p.loader = vec_in ? kDefaultVecLoader : PLAN_LOAD_ELEM;
-    if (o.loader >= 0 && (vec_in || o.loader == PLAN_LOAD_ELEM))
-        p.loader = o.loader;
+    p.loader = loader;
+    p.a_mn = ld.a_mn;
+    p.b_mn = ld.b_mn;
+    p.layout = layout;
     p.vec_out = vec_out;
     p.group_m = tile == TILE_256 ? 4 : 8;
     if (o.group >= 1)
@@ -278,14 +307,15 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
     }
     snprintf(buf, (size_t)buflen,
              "tile=%dx%dx%d stages=%d waves=%dx%d mfma=%dx%d sched=%s "
-             "loader=%s split=%d k_split=%lld vec_out=%d group_m=%d "
-             "grid=%lld",
+             "loader=%s a_along=%s b_along=%s split=%d k_split=%lld "
+             "vec_out=%d group_m=%d grid=%lld",
              p.bm, p.bn, kTileBK[p.tile], kTileStages[p.tile],
              kTileWM[p.tile], kTileWN[p.tile], kTileMfma[p.tile],
              kTileMfma[p.tile],
              p.loader == PLAN_LOAD_DIRECT ? scheds[kTileSched[p.tile]]
                                           : "staged",
-             loaders[p.loader], p.splits,
+             loaders[p.loader], p.a_mn ? "m" : "k", p.b_mn ? "n" : "k",
+             p.splits,
              (long long)p.k_split, p.vec_out ? 1 : 0, p.group_m,
              (long long)p.grid);
     return p.status;

@@ -3,13 +3,14 @@
 
 namespace gtn {
 
-hipError_t launch_tile64(const GemmArgs &a, int loader, bool out_f32,
-                         bool split, bool vec_out, unsigned grid,
-                         hipStream_t s)
+hipError_t launch_tile64(const GemmArgs &a, int loader, int layout,
+                         bool out_f32, bool split, bool vec_out,
+                         unsigned grid, hipStream_t s)
 {
     return launch_tile<64, 64, GTN_T64_BK, 2, 2, GTN_T64_STAGES, 2, 0,
-                       GTN_T64_MFMA>(
-        a, loader, out_f32, split, vec_out, grid, s);
+                       GTN_T64_MFMA, GTN_T64_DIRECT_LAYS,
+                       GTN_T64_ELEM_LAYS>(
+        a, loader, layout, out_f32, split, vec_out, grid, s);
 }
 
 }  // namespace gtn

@@ -141,8 +141,21 @@ def test_layout_checks(args, status):
                                    (ROW_MN, ROW_MN)])
 def test_operands_stored_along_m_or_n_are_planned(la, lb):
     # lda >= M for A stored K x M (here M = 300 > K = 64 is fine)
+    # rows of 8-element multiples: direct loader with transposing LDS
+    # reads; the 256-wide tile takes one operand stored along M / N
+    p = describe(1, 4096, 4096, 4096, layouts=(la, lb))
+    assert p["loader"] == "direct"
+    assert p["tile"].startswith("128x128" if la and lb else "256x256")
+    assert (p["a_along"], p["b_along"]) == ("m" if la else "k",
+                                            "n" if lb else "k")
+    # M = 300 is not a multiple of 8: an A stored along M needs the element
+    # loader (its last 16-byte chunk would read past row end)
     p = describe(1, 300, 200, 64, layouts=(la, lb))
-    assert p["loader"] == "elem"      # element loader for these layouts
+    assert p["loader"] == ("elem" if la else "direct")
+    # the element loader has no kernels for these layouts on 256 x 256
+    p = describe(1, 4000, 4000, 4096, layouts=(la, lb), lds=(
+        4003 if la else 4096, 4003 if lb else 4096, 4000, 4000))
+    assert p["loader"] == "elem" and p["tile"].startswith("128x128")
     # a row stride that only covers K is too short for a row of M / N
     short = (64, 64, 200, 200)
     assert g.describe(1, 300, 200, 64, layouts=(la, lb), lds=short) \

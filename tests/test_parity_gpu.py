@@ -372,6 +372,11 @@ def test_binding_takes_row_slices():
 
 LAYOUT_CASES = [
     # batch, M, N, K, out, beta, row-stride padding of the stored A and B
+    # M, N and strides multiples of 8: direct loads, transposing LDS reads
+    (2, 256, 192, 320, "f16", 0.0, (8, 16)),
+    (1, 520, 392, 1000, "f32", 0.5, (0, 8)),     # K tail, ragged tiles
+    (1, 72, 136, 64, "f32", -1.0, (8, 0)),
+    # otherwise the element loader
     (2, 300, 260, 832, "f16", 0.0, (8, 3)),
     (1, 129, 200, 1000, "f32", -2.0, (0, 0)),
     (3, 70, 90, 37, "f32", 0.5, (5, 1)),

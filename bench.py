@@ -9,6 +9,10 @@ compute-bound 4096 x 4096 x 4096 product with fp16 D.  The timed region is
 K back-to-back calls on one stream, bracketed by device synchronisations,
 and timed with HIP events recorded on that same stream.  One JSON line goes
 to stdout; `--all` adds a table of every workload on stderr.
+
+The fp32 transpose of the pages is measured the same way with
+`--workload transpose_1024` (their 1024 x 1024 case) or `transpose_8192`
+(8192 x 8192, 512 MiB moved: past the 256 MB last-level cache, so HBM).
 """
 from __future__ import annotations
 
@@ -31,21 +35,37 @@ CSRC = os.path.join(ROOT, "dense_gemm_fp16_amd", "csrc")
 KERNEL_SOURCES = ("gemm_tn_kernels.hpp", "gemm_tn_config.hpp",
                   "gemm_tn_launch.hpp", "gemm_tn_tile256.hip",
                   "gemm_tn_tile128.hip", "gemm_tn_tile64.hip")
+TRANSPOSE_SOURCES = ("transpose.hip",)
+# fp32 transposes: name -> (batch, M, N)
+TRANSPOSES = {"transpose_1024": (1, 1024, 1024),
+              "transpose_8192": (1, 8192, 8192)}
 
 
-def kernel_fingerprint() -> str:
+def _sources(workload: str):
+    return TRANSPOSE_SOURCES if workload in TRANSPOSES else KERNEL_SOURCES
+
+
+def _kernel_names(workload: str):
+    """Names (substrings) of the kernels one call of the workload runs."""
+    if workload in TRANSPOSES:
+        return ("transpose_f32_kernel",)
+    return ("gemm_tn_kernel", "splitk_reduce")
+
+
+def kernel_fingerprint(workload: str = "c3_4096") -> str:
     """Hash of the kernel sources; a traffic figure measured on other
     sources does not describe the kernel being timed."""
     import hashlib
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in _sources(workload):
         h.update(f.encode())
         h.update(open(os.path.join(CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
 def traffic_path(workload: str) -> str:
-    return os.path.join(PROFILES, f"gemm_tn_{workload}_traffic.json")
+    prefix = "" if workload in TRANSPOSES else "gemm_tn_"
+    return os.path.join(PROFILES, f"{prefix}{workload}_traffic.json")
 
 
 def load_traffic(workload: str):
@@ -55,7 +75,7 @@ def load_traffic(workload: str):
     if not os.path.exists(p):
         return None
     t = json.load(open(p))
-    if t.get("fingerprint") != kernel_fingerprint():
+    if t.get("fingerprint") != kernel_fingerprint(workload):
         return None
     return t
 
@@ -67,6 +87,8 @@ def summarize_pmc(fetch_csv, write_csv, workload, cal_mib):
     import csv
     import statistics
 
+    wanted = _kernel_names(workload)
+
     def per_kernel(path, counter):
         gemm, copy = [], []
         for r in csv.DictReader(open(path)):
@@ -74,13 +96,13 @@ def summarize_pmc(fetch_csv, write_csv, workload, cal_mib):
                 continue
             v = float(r["Counter_Value"])
             name = r["Kernel_Name"]
-            if "gemm_tn_kernel" in name or "splitk_reduce" in name:
+            if any(k in name for k in wanted):
                 gemm.append((int(r["Dispatch_Id"]), name, v))
             elif "copy" in name.lower():
                 copy.append(v)
         return gemm, copy
 
-    out = {"workload": workload, "fingerprint": kernel_fingerprint(),
+    out = {"workload": workload, "fingerprint": kernel_fingerprint(workload),
            "calibration_mib": cal_mib}
     for key, path, counter in (("fetch", fetch_csv, "FETCH_SIZE"),
                                ("write", write_csv, "WRITE_SIZE")):
@@ -189,6 +211,84 @@ def cpu_baseline(w, target_s):
                       f"{platform.processor() or platform.machine()}"}
 
 
+def _transpose_input(batch, M, N, torch):
+    """Seeded uniform [-1, 1) fp32 values, drawn on the GPU (the values do
+    not change the copy's speed; the parity tests use the seeded host
+    generator)."""
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED0100 + M)
+    return torch.rand((batch, M, N), generator=gen, device="cuda") * 2 - 1
+
+
+def time_transpose(batch, M, N, steps, warmup):
+    import torch
+    import dense_gemm_fp16_amd as g
+    x = _transpose_input(batch, M, N, torch)
+    y = torch.empty((batch, N, M), device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.transpose_f32(x, out=y, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        g.transpose_f32(x, out=y, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def cpu_baseline_transpose(batch, M, N, target_s):
+    """The transpose oracle (one thread: it is numpy row copies) on the first
+    R rows of a host copy of the input, rate scaled to GB/s moved."""
+    from oracle import transpose as T
+    x = np.random.default_rng(0).random((1, M, N), dtype=np.float32)
+    rows, reps = min(M, 256), 1
+    while True:
+        t = time.perf_counter()
+        for _ in range(reps):
+            T.transpose(x[:, :rows])
+        dt = time.perf_counter() - t
+        if dt >= target_s / 4:
+            break
+        if rows < M:
+            rows = min(M, rows * 4)
+        else:
+            reps *= 4
+    return {"value": 8.0 * rows * N * reps / dt / 1e9, "unit": "GB/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{reps} x the first {rows} of {M} rows of the "
+                      f"{M}x{N} input ({dt:.2f} s)"}
+
+
+def transpose_main(a):
+    batch, M, N = TRANSPOSES[a.workload]
+    sec = time_transpose(batch, M, N, a.steps, a.warmup)
+    nbytes = 8.0 * batch * M * N
+    gbs = nbytes / sec / 1e9
+    t = load_traffic(a.workload)
+    line = {
+        "metric": f"fp32 transpose GB/s ({M}x{N}); % of MI355X HBM peak",
+        "value": round(gbs, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"transpose_f32_{M}x{N}"
+                               + (f"_batch{batch}" if batch > 1 else ""),
+                   "M": M, "N": N, "batch": batch},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4),
+                     "traffic": round(t["bytes_per_launch"]) if t else None},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_transpose(batch, M, N,
+                                                      a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def describe(w):
     import dense_gemm_fp16_amd as g
     return g.describe(w.batch, w.M, w.N, w.K, w.beta, w.out_dtype, True)
@@ -214,7 +314,6 @@ def main():
         sys.exit(2)
     import seeded_inputs as si
 
-    w = si.workload(a.workload)
     if a.copy_calibration_mib:
         n = a.copy_calibration_mib * 1024 * 1024 // 4
         src = torch.ones(n, device="cuda")
@@ -222,6 +321,10 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.workload in TRANSPOSES:
+        transpose_main(a)
+        return
+    w = si.workload(a.workload)
     sec = time_workload(w, a.steps, a.warmup)
     tflops = w.flops / sec / 1e12
     gbs = w.algorithmic_bytes / sec / 1e9
@@ -238,8 +341,11 @@ def main():
     t = load_traffic(a.workload)
     roof["traffic"] = round(t["bytes_per_launch"]) if t else None
     line = {
-        "metric": "GEMM TFLOP/s (fp16 in, fp32 acc) at 4096^3; "
-                  "% of MI355X fp16 MFMA peak",
+        "metric": (f"GEMM TFLOP/s (fp16 in, fp32 acc) at "
+                   + ("4096^3" if a.workload == "c3_4096"
+                      else f"{w.M}x{w.N}x{w.K}" + (
+                          f" batch {w.batch}" if w.batch > 1 else ""))
+                   + "; % of MI355X fp16 MFMA peak"),
         "value": round(tflops, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -270,6 +376,12 @@ def main():
             gb = wx.algorithmic_bytes / s / 1e9
             print(f"{name:<14}{describe(wx):<60}{s * 1e6:>10.2f}{tf:>10.1f}"
                   f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
+                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+        for name, (batch, M, N) in TRANSPOSES.items():
+            s = time_transpose(batch, M, N, a.steps, a.warmup)
+            gb = 8.0 * batch * M * N / s / 1e9
+            print(f"{name:<14}{'fp32 transpose, 64x64 tiles':<60}"
+                  f"{s * 1e6:>10.2f}{'-':>10}{'-':>8}{gb:>9.0f}"
                   f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)

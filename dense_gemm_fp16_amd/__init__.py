@@ -34,7 +34,8 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(5)
 import torch  # noqa: E402,F401
 
 EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_ex",
-           "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version")
+           "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version",
+           "transpose_f32")
 
 _REBUILD = ("run `python dense_gemm_fp16_amd/build.py` "
             "(or __graft_entry__.build()) first")
@@ -63,6 +64,8 @@ _lib.gemm_tn_describe.restype = _int
 _lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _int, _i64, _int,
                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64,
                                   _f32, _int, _int, ctypes.c_char_p, _i64]
+_lib.transpose_f32.restype = _int
+_lib.transpose_f32.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp]
 _lib.gemm_tn_status_string.restype = ctypes.c_char_p
 _lib.gemm_tn_status_string.argtypes = [_int]
 _lib.gemm_tn_version.restype = _int
@@ -240,3 +243,32 @@ def gemm_tn_ex(batch, M, N, K, alpha, A_ptr, lda, strideA, B_ptr, ldb,
                            strideA, B_ptr, layout_b, ldb, strideB,
                            float(beta), C_ptr, ldc, strideC, D_ptr, ldd,
                            strideD, d_dtype, stream_handle)
+
+
+def transpose_f32(x, out=None, stream=None):
+    """y = x^T for a contiguous float32 (M, N) or (batch, M, N) GPU tensor
+    (include/transpose_f32.h); returns y of shape (N, M) or (batch, N, M)."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
+        raise ValueError("x must be a contiguous float32 GPU tensor")
+    if x.dim() not in (2, 3):
+        raise ValueError("x must be 2-D or 3-D")
+    batch = x.shape[0] if x.dim() == 3 else 1
+    M, N = x.shape[-2], x.shape[-1]
+    shape = (N, M) if x.dim() == 2 else (batch, N, M)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float32, device=x.device)
+    if (tuple(out.shape) != shape or out.dtype != torch.float32
+            or not out.is_contiguous() or not out.is_cuda):
+        raise ValueError(f"out must be a contiguous float32 GPU tensor "
+                         f"of shape {shape}")
+    st = _lib.transpose_f32(batch, M, N, x.data_ptr(), out.data_ptr(),
+                            _stream_handle(stream))
+    if st != OK:
+        raise GemmError(st)
+    return out
+
+
+def transpose_f32_raw(batch, M, N, x_ptr, y_ptr, stream_handle) -> int:
+    """Raw-pointer call of transpose_f32(); returns the status code."""
+    return _lib.transpose_f32(batch, M, N, x_ptr, y_ptr, stream_handle)

@@ -586,21 +586,17 @@ gemm_tn_kernel(GemmArgs p)
         constexpr int CR = W / 8;
         const int i = lane & 15, g = lane >> 4;
         const int col = c0 + 4 * (i & 3);
-        half8 out;
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
+        auto rd = [&](int r) {
             const int row = ks * 32 + 8 * g + 4 * r + (i >> 2);
             const int pc = swizzle_mn<CR>(row, col >> 3);
             const GTN_LDS _Float16 *a = (const GTN_LDS _Float16 *)s +
                                         row * W + pc * 8 + (col & 7);
-            const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (GTN_LDS s16x4 *)a);
-            const half4 h = __builtin_bit_cast(half4, v);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                out[4 * r + e] = h[e];
-        }
-        return out;
+            return __builtin_bit_cast(
+                half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                           (GTN_LDS s16x4 *)a));
+        };
+        const half4 lo = rd(0), hi = rd(1);
+        return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     };
     // Fragments are read in the order the MFMAs below consume them (B0, A0,
     // then B1.., then A1..), so the first MFMAs of a k-step depend only on

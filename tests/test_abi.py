@@ -8,7 +8,9 @@ import re
 import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "gemm_tn.h")
+HEADERS = [os.path.join(ROOT, "include", h)
+           for h in sorted(os.listdir(os.path.join(ROOT, "include")))
+           if h.endswith(".h")]
 
 g = pytest.importorskip("dense_gemm_fp16_amd")
 
@@ -21,10 +23,12 @@ S = ctypes.c_void_p(0)
 
 
 def declared_functions():
-    text = open(HEADER).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(gemm_tn\w*)\s*\(", text,
-                                 flags=re.M)))
+    names = set()
+    for h in HEADERS:
+        text = re.sub(r"/\*.*?\*/", "", open(h).read(), flags=re.S)
+        names |= set(re.findall(r"^(?:int|const char \*)\s*(\w+)\s*\(", text,
+                                flags=re.M))
+    return sorted(names)
 
 
 def test_exports_every_declared_symbol():
@@ -213,3 +217,24 @@ def test_override_spec(monkeypatch):
     # a vector loader is refused when alignment does not allow it
     p = describe(1, 512, 512, 1000 + 3)
     assert p["loader"] == "elem"
+
+
+@pytest.mark.parametrize("args,status", [
+    ((-1, 4, 4), INVALID), ((1, -4, 4), INVALID), ((1, 4, -4), INVALID),
+    ((2 ** 40, 2 ** 20, 2 ** 20), INVALID),            # size overflow
+    ((1, 2 ** 23 + 4, 8), UNSUPPORTED), ((1, 8, 2 ** 23 + 4), UNSUPPORTED),
+    ((0, 4, 4), OK), ((3, 0, 4), OK), ((3, 4, 0), OK),  # nothing to do
+])
+def test_transpose_argument_checks(args, status):
+    batch, M, N = args
+    # distinct dummy buffers far apart: the checks never touch them
+    assert g.transpose_f32_raw(batch, M, N, ctypes.c_void_p(0x1000),
+                               ctypes.c_void_p(0x1000 + 2 ** 62), S) == status
+
+
+def test_transpose_rejects_overlap_and_null():
+    x = ctypes.c_void_p(0x100000)
+    assert g.transpose_f32_raw(1, 4, 4, x, ctypes.c_void_p(0x100000 + 60),
+                               S) == INVALID          # 64-byte ranges overlap
+    assert g.transpose_f32_raw(1, 4, 4, None, x, S) == INVALID
+    assert g.transpose_f32_raw(1, 4, 4, x, None, S) == INVALID

@@ -1,4 +1,4 @@
-"""Seeded synthetic inputs for the fp16 TN GEMM workloads.
+"""Seeded synthetic inputs for the fp16 TN GEMM and attention workloads.
 
 This module is shared by the tests, the benchmark and the smoke check.  It
 holds no GEMM arithmetic: it only turns a seed into fp16 / fp32 tensors of
@@ -28,6 +28,7 @@ _M1 = np.uint64(0xBF58476D1CE4E5B9)
 _M2 = np.uint64(0x94D049BB133111EB)
 
 TENSOR_A, TENSOR_B, TENSOR_C = 0, 1, 2
+TENSOR_Q, TENSOR_K, TENSOR_V = 3, 4, 5
 
 
 def mix64(z: np.ndarray) -> np.ndarray:
@@ -164,3 +165,56 @@ def workload(name: str, int_values: bool = False) -> Workload:
         seed += 0x10      # 4a and 4b share a workload number
     return build(name + ("_int" if int_values else ""), scale=scale,
                  kind=kind, seed=seed, **cfg)
+
+
+@dataclass
+class AttentionWorkload:
+    """One attention forward problem, O = softmax(scale * Q K^T) V, over
+    `batch` independent heads."""
+    name: str
+    batch: int
+    Lq: int
+    Lk: int
+    d: int
+    scale: float
+    out_dtype: str                      # "f16" or "f32"
+    Q: np.ndarray = field(repr=False)   # (batch, Lq, d) float16
+    K: np.ndarray = field(repr=False)   # (batch, Lk, d) float16
+    V: np.ndarray = field(repr=False)   # (batch, Lk, d) float16
+
+    @property
+    def flops(self) -> int:
+        """The two products: 2 * Lq * Lk * d for the scores, as many for
+        P V."""
+        return 4 * self.batch * self.Lq * self.Lk * self.d
+
+    @property
+    def algorithmic_bytes(self) -> int:
+        es = 2 if self.out_dtype == "f16" else 4
+        return self.batch * self.d * (2 * (self.Lq + 2 * self.Lk)
+                                      + es * self.Lq)
+
+
+# Attention workloads: the score product of the head-dimension-64 study
+# (64 heads of 1024 queries and keys) completed into the forward pass, and
+# a small ragged case.  Q, K and V are standard normal, as the score
+# product's operands are.
+ATTENTION_WORKLOADS = {
+    "attn_small": dict(batch=2, Lq=200, Lk=300, d=64, scale=0.125,
+                       out_dtype="f16", num=0x61),
+    "attn_64x1024": dict(batch=64, Lq=1024, Lk=1024, d=64, scale=0.125,
+                         out_dtype="f16", num=0x62),
+}
+
+
+def attention_workload(name: str, out_dtype: str | None = None,
+                       magnitude: float = 1.0) -> AttentionWorkload:
+    cfg = dict(ATTENTION_WORKLOADS[name])
+    seed = SEED_BASE + cfg.pop("num")
+    if out_dtype is not None:
+        cfg["out_dtype"] = out_dtype
+    b, Lq, Lk, d = cfg["batch"], cfg["Lq"], cfg["Lk"], cfg["d"]
+    Q = make("normal", (b, Lq, d), seed, TENSOR_Q, np.float16, magnitude)
+    K = make("normal", (b, Lk, d), seed, TENSOR_K, np.float16, magnitude)
+    V = make("normal", (b, Lk, d), seed, TENSOR_V, np.float16)
+    return AttentionWorkload(name, Q=Q, K=K, V=V, **cfg)

@@ -45,3 +45,17 @@ def test_workload_shapes():
     wi = si.workload("c2_1024", int_values=True)
     assert set(np.unique(wi.A.astype(np.float64))) <= set(range(-3, 4))
     assert wi.flops == 2 * 1024 ** 3
+
+
+def test_attention_workloads_are_seeded_and_shaped():
+    import seeded_inputs as si
+    w1 = si.attention_workload("attn_small")
+    w2 = si.attention_workload("attn_small")
+    assert w1.Q.shape == (2, 200, 64) and w1.K.shape == (2, 300, 64)
+    assert w1.V.shape == (2, 300, 64) and w1.Q.dtype == np.float16
+    for x, y in ((w1.Q, w2.Q), (w1.K, w2.K), (w1.V, w2.V)):
+        assert np.array_equal(x.view(np.uint16), y.view(np.uint16))
+    # Q, K and V come from distinct streams
+    assert not np.array_equal(w1.K, w1.V)
+    assert abs(float(w1.V.astype(np.float64).std()) - 1.0) < 0.05
+    assert w1.flops == 4 * 2 * 200 * 300 * 64

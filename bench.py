@@ -13,6 +13,9 @@ to stdout; `--all` adds a table of every workload on stderr.
 The fp32 transpose of the pages is measured the same way with
 `--workload transpose_1024` (their 1024 x 1024 case) or `transpose_8192`
 (8192 x 8192, 512 MiB moved: past the 256 MB last-level cache, so HBM).
+The attention forward pass O = softmax(scale Q K^T) V runs with
+`--workload attn_64x1024` (64 heads of 1024 queries and keys, d = 64: the
+score product completed into the forward pass) or `attn_small`.
 """
 from __future__ import annotations
 
@@ -36,19 +39,28 @@ KERNEL_SOURCES = ("gemm_tn_kernels.hpp", "gemm_tn_config.hpp",
                   "gemm_tn_launch.hpp", "gemm_tn_tile256.hip",
                   "gemm_tn_tile128.hip", "gemm_tn_tile64.hip")
 TRANSPOSE_SOURCES = ("transpose.hip",)
+ATTENTION_SOURCES = ("attention_fwd.hip", "gemm_tn_kernels.hpp",
+                     "gemm_tn_config.hpp")
+ATTENTIONS = ("attn_64x1024", "attn_small")
 # fp32 transposes: name -> (batch, M, N)
 TRANSPOSES = {"transpose_1024": (1, 1024, 1024),
               "transpose_8192": (1, 8192, 8192)}
 
 
 def _sources(workload: str):
-    return TRANSPOSE_SOURCES if workload in TRANSPOSES else KERNEL_SOURCES
+    if workload in TRANSPOSES:
+        return TRANSPOSE_SOURCES
+    if workload in ATTENTIONS:
+        return ATTENTION_SOURCES
+    return KERNEL_SOURCES
 
 
 def _kernel_names(workload: str):
     """Names (substrings) of the kernels one call of the workload runs."""
     if workload in TRANSPOSES:
         return ("transpose_f32_kernel",)
+    if workload in ATTENTIONS:
+        return ("attn_fwd_kernel",)
     return ("gemm_tn_kernel", "splitk_reduce")
 
 
@@ -64,7 +76,8 @@ def kernel_fingerprint(workload: str = "c3_4096") -> str:
 
 
 def traffic_path(workload: str) -> str:
-    prefix = "" if workload in TRANSPOSES else "gemm_tn_"
+    prefix = "" if workload in TRANSPOSES or workload in ATTENTIONS \
+        else "gemm_tn_"
     return os.path.join(PROFILES, f"{prefix}{workload}_traffic.json")
 
 
@@ -262,6 +275,90 @@ def cpu_baseline_transpose(batch, M, N, target_s):
                       f"{M}x{N} input ({dt:.2f} s)"}
 
 
+def _attention_inputs(w, torch):
+    return [torch.from_numpy(x).cuda() for x in (w.Q, w.K, w.V)]
+
+
+def time_attention(w, steps, warmup):
+    """Average time of one attention_fwd call (seconds), HIP events on the
+    launch stream; the seeded inputs are resident in HBM."""
+    import torch
+    import dense_gemm_fp16_amd as g
+    q, k, v = _attention_inputs(w, torch)
+    dt = torch.float16 if w.out_dtype == "f16" else torch.float32
+    o = torch.empty(q.shape, dtype=dt, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.attention_fwd(q, k, v, w.scale, out=o, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        g.attention_fwd(q, k, v, w.scale, out=o, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def cpu_baseline_attention(w, target_s):
+    """The attention oracle (float64 numpy; its products run on the BLAS
+    threads) over the first H heads, repeated until the run takes about a
+    quarter of target_s; rate scaled to TFLOP/s of the workload's count."""
+    from oracle import attention as AT
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()]
+                    or [1])
+    except Exception:                       # noqa: BLE001
+        cores = 1
+    heads, reps = 1, 1
+    while True:
+        t = time.perf_counter()
+        for _ in range(reps):
+            AT.attention(w.Q[:heads], w.K[:heads], w.V[:heads], w.scale)
+        dt = time.perf_counter() - t
+        if dt >= target_s / 4:
+            break
+        if heads < w.batch:
+            heads = min(w.batch, heads * 4)
+        else:
+            reps *= 2
+    flops = 4.0 * heads * reps * w.Lq * w.Lk * w.d
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{reps} x the first {heads} of {w.batch} heads "
+                      f"({w.Lq}x{w.Lk}x{w.d}, float64 numpy), {dt:.2f} s"}
+
+
+def attention_main(a):
+    import seeded_inputs as si
+    w = si.attention_workload(a.workload)
+    sec = time_attention(w, a.steps, a.warmup)
+    tflops = w.flops / sec / 1e12
+    t = load_traffic(a.workload)
+    line = {
+        "metric": (f"attention forward TFLOP/s ({w.batch} heads, "
+                   f"{w.Lq} queries x {w.Lk} keys, d {w.d}; fp16 in, fp32 "
+                   f"acc); % of MI355X fp16 MFMA peak"),
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"attention_fwd_{w.batch}x{w.Lq}x{w.Lk}x{w.d}",
+                   "batch": w.batch, "Lq": w.Lq, "Lk": w.Lk, "d": w.d,
+                   "scale": w.scale, "out": w.out_dtype},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4),
+                     "traffic": round(t["bytes_per_launch"]) if t else None},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_attention(w, a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def transpose_main(a):
     batch, M, N = TRANSPOSES[a.workload]
     sec = time_transpose(batch, M, N, a.steps, a.warmup)
@@ -324,6 +421,9 @@ def main():
     if a.workload in TRANSPOSES:
         transpose_main(a)
         return
+    if a.workload in ATTENTIONS:
+        attention_main(a)
+        return
     w = si.workload(a.workload)
     sec = time_workload(w, a.steps, a.warmup)
     tflops = w.flops / sec / 1e12
@@ -375,6 +475,15 @@ def main():
             tf = wx.flops / s / 1e12
             gb = wx.algorithmic_bytes / s / 1e9
             print(f"{name:<14}{describe(wx):<60}{s * 1e6:>10.2f}{tf:>10.1f}"
+                  f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
+                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+        for name in ATTENTIONS:
+            wa = si.attention_workload(name)
+            s = time_attention(wa, a.steps, a.warmup)
+            tf = wa.flops / s / 1e12
+            gb = wa.algorithmic_bytes / s / 1e9
+            print(f"{name:<14}{'attention forward, 128 queries x 64 keys':<60}"
+                  f"{s * 1e6:>10.2f}{tf:>10.1f}"
                   f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
                   f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
         for name, (batch, M, N) in TRANSPOSES.items():

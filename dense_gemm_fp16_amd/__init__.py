@@ -35,7 +35,7 @@ import torch  # noqa: E402,F401
 
 EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_ex",
            "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version",
-           "transpose_f32")
+           "transpose_f32", "attention_fwd")
 
 _REBUILD = ("run `python dense_gemm_fp16_amd/build.py` "
             "(or __graft_entry__.build()) first")
@@ -66,6 +66,9 @@ _lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _int, _i64, _int,
                                   _f32, _int, _int, ctypes.c_char_p, _i64]
 _lib.transpose_f32.restype = _int
 _lib.transpose_f32.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp]
+_lib.attention_fwd.restype = _int
+_lib.attention_fwd.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp,
+                               _vp, _int, _vp, _vp]
 _lib.gemm_tn_status_string.restype = ctypes.c_char_p
 _lib.gemm_tn_status_string.argtypes = [_int]
 _lib.gemm_tn_version.restype = _int
@@ -272,3 +275,58 @@ def transpose_f32(x, out=None, stream=None):
 def transpose_f32_raw(batch, M, N, x_ptr, y_ptr, stream_handle) -> int:
     """Raw-pointer call of transpose_f32(); returns the status code."""
     return _lib.transpose_f32(batch, M, N, x_ptr, y_ptr, stream_handle)
+
+
+def attention_fwd(q, k, v, scale: float, out=None, out_dtype=None,
+                  return_lse: bool = False, lse=None, stream=None):
+    """O = softmax(scale * q k^T) v per head (include/attention_fwd.h).
+
+    q: (Lq, d) or (batch, Lq, d), k and v: (Lk, d) or (batch, Lk, d), all
+    contiguous float16 GPU tensors with d = 64.  out: optional contiguous
+    tensor of q's shape, float16 (default) or float32.  With return_lse (or
+    a float32 `lse` tensor of shape (batch, Lq) / (Lq,)), the natural
+    log-sum-exp of each row of scale * q k^T is written too and (O, lse) is
+    returned; otherwise O."""
+    torch = _torch()
+    for t, n in ((q, "q"), (k, "k"), (v, "v")):
+        if (t.dtype != torch.float16 or not t.is_cuda
+                or not t.is_contiguous() or t.dim() not in (2, 3)):
+            raise ValueError(f"{n} must be a contiguous 2-D or 3-D float16 "
+                             f"GPU tensor")
+    if not (q.dim() == k.dim() == v.dim()):
+        raise ValueError("q, k and v need the same number of dimensions")
+    batch = q.shape[0] if q.dim() == 3 else 1
+    Lq, d = q.shape[-2], q.shape[-1]
+    Lk = k.shape[-2]
+    if (k.shape[-1] != d or tuple(v.shape) != tuple(k.shape)
+            or (q.dim() == 3 and k.shape[0] != batch)):
+        raise ValueError("k and v must be (batch, Lk, d) with q's batch and d")
+    if out is None:
+        out = torch.empty(q.shape, dtype=out_dtype or torch.float16,
+                          device=q.device)
+    if (tuple(out.shape) != tuple(q.shape) or not out.is_cuda
+            or not out.is_contiguous()):
+        raise ValueError("out must be a contiguous GPU tensor of q's shape")
+    lse_shape = tuple(q.shape[:-1])
+    if lse is None and return_lse:
+        lse = torch.empty(lse_shape, dtype=torch.float32, device=q.device)
+    if lse is not None and (tuple(lse.shape) != lse_shape
+                            or lse.dtype != torch.float32 or not lse.is_cuda
+                            or not lse.is_contiguous()):
+        raise ValueError(f"lse must be a contiguous float32 GPU tensor of "
+                         f"shape {lse_shape}")
+    st = _lib.attention_fwd(batch, Lq, Lk, d, float(scale), q.data_ptr(),
+                            k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                            _dtype_code(out.dtype),
+                            lse.data_ptr() if lse is not None else None,
+                            _stream_handle(stream))
+    if st != OK:
+        raise GemmError(st)
+    return (out, lse) if lse is not None else out
+
+
+def attention_fwd_raw(batch, Lq, Lk, d, scale, q_ptr, k_ptr, v_ptr, o_ptr,
+                      o_dtype, lse_ptr, stream_handle) -> int:
+    """Raw-pointer call of attention_fwd(); returns the status code."""
+    return _lib.attention_fwd(batch, Lq, Lk, d, float(scale), q_ptr, k_ptr,
+                              v_ptr, o_ptr, o_dtype, lse_ptr, stream_handle)

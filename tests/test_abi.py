@@ -238,3 +238,34 @@ def test_transpose_rejects_overlap_and_null():
                                S) == INVALID          # 64-byte ranges overlap
     assert g.transpose_f32_raw(1, 4, 4, None, x, S) == INVALID
     assert g.transpose_f32_raw(1, 4, 4, x, None, S) == INVALID
+
+
+def _attn(batch=2, Lq=8, Lk=8, d=64, scale=0.125, o_dtype=F16, lse=None,
+          q=0x10000, k=0x20000, v=0x30000, o=0x40000):
+    ptr = lambda a: ctypes.c_void_p(a) if a is not None else None
+    return g.attention_fwd_raw(batch, Lq, Lk, d, scale, ptr(q), ptr(k),
+                               ptr(v), ptr(o), o_dtype, ptr(lse), S)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(batch=-1), INVALID), (dict(Lq=-1), INVALID), (dict(Lk=-1), INVALID),
+    (dict(d=-1), INVALID), (dict(o_dtype=7), INVALID),
+    (dict(scale=float("inf")), INVALID), (dict(scale=float("nan")), INVALID),
+    (dict(Lk=0), INVALID),                       # softmax over no keys
+    (dict(q=None), INVALID), (dict(k=None), INVALID), (dict(v=None), INVALID),
+    (dict(o=None), INVALID),
+    (dict(o=0x10000 + 16), INVALID),             # O overlaps Q
+    (dict(o=0x30000 + 2048 - 16), INVALID),      # O overlaps V's tail
+    (dict(lse=0x40000 + 8), INVALID),            # lse overlaps O
+    (dict(batch=2 ** 40, Lq=2 ** 20), INVALID),  # size overflow
+    (dict(d=128), UNSUPPORTED), (dict(d=32), UNSUPPORTED),
+    (dict(Lk=2 ** 23 + 1, k=0x10 ** 12, v=0x20 ** 12, o=0x30 ** 12),
+     UNSUPPORTED),
+    (dict(q=0x10008), UNSUPPORTED),              # not 16-byte aligned
+    (dict(o=0x40004), UNSUPPORTED),
+    (dict(lse=0x50002), UNSUPPORTED),
+    (dict(batch=0), OK), (dict(Lq=0), OK),       # nothing to do
+    (dict(batch=0, Lk=0), OK), (dict(Lq=0, q=None, o=None), OK),
+])
+def test_attention_argument_checks(kw, status):
+    assert _attn(**kw) == status

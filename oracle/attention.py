@@ -26,7 +26,8 @@ acceptance bound below.
 Acceptance bound (`bounds`): a first-order bound on the error of a kernel
 that forms S in fp32 from exact fp16 products, computes the exponentials in
 fp32 with a per-row shift, rounds the probabilities to fp16 for the P V
-product, accumulates in fp32, and divides by the fp32 row sum at the end;
+product, accumulates in fp32, and divides at the end by the row sum (an
+fp32 sum of the probabilities, taken before or after their fp16 rounding);
 doubled for second-order terms.  Its derivation is written out at `bounds`.
 
 Pins (tests/test_oracle_attention.py): a hand-worked example under
@@ -91,9 +92,14 @@ def bounds(Q, K, V, scale: float):
     PA = sum_j p_j A_j, WA = sum_j p_j A_j |v_j|, c = |scale| * log2(e),
     u = 2^-24 (fp32 unit roundoff), and Lk, d the key count and head
     dimension.  To first order the kernel's weight of key j is
-    p_j (1 + delta_j + theta_j - theta_bar - eta), where
+    p_j (1 + delta_j - delta_bar + theta_j - theta_bar - eta), where
       delta_j : fp16 rounding of the probability, |delta_j| <= 2^-11 (an
                 absolute 2^-25 / l below fp16's normal range, l >= 1);
+      delta_bar : the same roundings averaged into the row sum, when the
+                sum is formed from the rounded probabilities (0 when it is
+                formed in fp32 before rounding); sum_j p_j (delta_j -
+                delta_bar) v_j = sum_j p_j delta_j (v_j - o), bounded by
+                2^-11 (W + |o|) either way (o the exact output);
       theta_j : fp32 score error, |S_j error| <= (d - 1) u A_j, scaled by
                 c ln 2 through exp2, plus the exp2 / shift roundings;
       theta_bar : the same errors averaged into the row sum;
@@ -101,11 +107,11 @@ def bounds(Q, K, V, scale: float):
     and the fp32 P V accumulation adds at most Lk u W, each rescale of the
     accumulator by a new row maximum about 2^-22 (at most Lk / 64 + 8 of
     them).  Summing |weight error| |v_j| over j:
-      B = W (2^-11 + 2 Lk u + (Lk/64 + 8) 2^-22)
+      B = 2^-11 (W + |o|) + W (2 Lk u + (Lk/64 + 8) 2^-22)
           + ln2 c (d - 1) u (WA + PA W) + Lk 2^-25 max|v|.
-    tol_O = 2 B covers the second-order terms.  The log-sum-exp carries no
-    fp16 rounding: tol_lse = 2 (Lk u + ln2 c (d - 1) u PA + 2^-19)
-    + 2^-22 |lse|."""
+    tol_O = 2 B covers the second-order terms.  The log-sum-exp carries the
+    row sum's relative error (delta_bar, theta_bar, eta) as an absolute one:
+    tol_lse = 2 (2^-11 + Lk u + ln2 c (d - 1) u PA + 2^-19) + 2^-22 |lse|."""
     Q, K, V, two_d = _batched(Q, K, V)
     batch, Lq, d = Q.shape
     Lk = K.shape[1]
@@ -123,12 +129,15 @@ def bounds(Q, K, V, scale: float):
         PA = (P * A).sum(axis=1, keepdims=True)
         WA = (P * A) @ Va
         score = math.log(2.0) * c * (d - 1) * u
-        B = (W * (2.0 ** -11 + 2 * Lk * u + (Lk / 64 + 8) * 2.0 ** -22)
+        O = P @ V[b]
+        B = (2.0 ** -11 * (W + np.abs(O))
+             + W * (2 * Lk * u + (Lk / 64 + 8) * 2.0 ** -22)
              + score * (WA + PA * W)
              + Lk * 2.0 ** -25 * (Va.max() if Va.size else 0.0))
         tol_O[b] = 2.0 * B
         lse = S.max(axis=1) + np.log(E.sum(axis=1))
-        tol_lse[b] = (2.0 * (Lk * u + score * PA[:, 0] + 2.0 ** -19)
+        tol_lse[b] = (2.0 * (2.0 ** -11 + Lk * u + score * PA[:, 0]
+                             + 2.0 ** -19)
                       + 2.0 ** -22 * np.abs(lse))
     return (tol_O[0], tol_lse[0]) if two_d else (tol_O, tol_lse)
 

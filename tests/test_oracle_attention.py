@@ -159,9 +159,10 @@ def test_zero_keys_is_rejected():
 # ---- the acceptance bound -------------------------------------------------
 
 def _emulate(Q, K, V, scale, block=64, threshold=8.0, skip_rescale=False,
-             pad_to_block=False):
+             pad_to_block=False, rounded_sum=False):
     """A float32 model of a blocked kernel: fp32 scores, exp2 with a lazily
-    updated per-row shift, fp16 probabilities for P V, fp32 sums.  With
+    updated per-row shift, fp16 probabilities for P V, fp32 sums (of the
+    fp16 probabilities with `rounded_sum`, else of the fp32 ones).  With
     `skip_rescale` the accumulator is not rescaled when the shift moves (a
     planted mistake); with `pad_to_block` the zero keys that pad the last
     block are not masked (another one)."""
@@ -197,8 +198,9 @@ def _emulate(Q, K, V, scale, block=64, threshold=8.0, skip_rescale=False,
                     l *= f
                     m = mn
             p = np.exp2(s - m[:, None]).astype(np.float32)
-            l += p.sum(axis=1, dtype=np.float32)
-            acc += p.astype(np.float16).astype(np.float32) @ v
+            p16 = p.astype(np.float16).astype(np.float32)
+            l += (p16 if rounded_sum else p).sum(axis=1, dtype=np.float32)
+            acc += p16 @ v
         O[b] = acc / l[:, None]
         lse[b] = m * np.float32(math.log(2.0)) + np.log(l)
     return O, lse
@@ -210,12 +212,13 @@ def _emulate(Q, K, V, scale, block=64, threshold=8.0, skip_rescale=False,
 def test_bound_accepts_a_float32_kernel_model(shape, scale, mag):
     batch, Lq, Lk, d = shape
     Q, K, V = _inputs(batch, Lq, Lk, d, 12, scale=mag)
-    O, lse = _emulate(Q, K, V, scale)
-    for out in ("f32", "f16"):
-        Oo = O if out == "f32" else O.astype(np.float16)
-        r = AT.check(Oo, lse, Q, K, V, scale, out)
-        assert r["O_fail"] == 0 and r["lse_fail"] == 0, r
-        assert r["O_ratio"] < 0.5, r      # the bound is not tight
+    for rounded in (False, True):
+        O, lse = _emulate(Q, K, V, scale, rounded_sum=rounded)
+        for out in ("f32", "f16"):
+            Oo = O if out == "f32" else O.astype(np.float16)
+            r = AT.check(Oo, lse, Q, K, V, scale, out)
+            assert r["O_fail"] == 0 and r["lse_fail"] == 0, r
+            assert r["O_ratio"] < 0.5, r      # the bound is not tight
 
 
 def test_bound_rejects_planted_mistakes():

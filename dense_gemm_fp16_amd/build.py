@@ -34,13 +34,23 @@ FLAGS = [
 ]
 
 
+# Per-file flags.  The attention kernel applies vector ALU work (the softmax,
+# the rescale by a new row maximum) to MFMA results; with the MFMA operands
+# and results in ordinary VGPRs instead of accumulation registers, none of
+# that costs a copy between the two register files.
+FILE_FLAGS = {
+    "attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+}
+
+
 def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC)
                   if f.endswith(".hip"))
 
 
 def _compile(src, obj, extra):
-    cmd = [HIPCC] + FLAGS + extra + ["-c", src, "-o", obj]
+    cmd = ([HIPCC] + FLAGS + FILE_FLAGS.get(os.path.basename(src), [])
+           + extra + ["-c", src, "-o", obj])
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,
                        text=True)
     # hipcc's host pass does not know the device-only feature; drop that note

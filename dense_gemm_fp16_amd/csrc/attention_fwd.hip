@@ -16,14 +16,18 @@
 //  * Q: each wave loads its fragments once, straight from HBM into
 //    registers (16 bytes per lane per 32-wide d-step).
 //  * K, V: per key block, a 64 x 64 K tile and V tile go into LDS through
-//    direct 16-byte buffer loads (two stages: block kb+1 loads while kb is
-//    computed).  Keys past Lk read as zero.
+//    direct 16-byte buffer loads, two stages each.  Keys past Lk read as
+//    zero.  The loop is software-pipelined: while the softmax of block kb
+//    runs on the vector ALU, the MFMAs form the scores of block kb + 1, so
+//    the K tiles run one block ahead of the V tiles.
 //  * S = Q K^T: v_mfma_f32_16x16x32_f16 with the K fragment as the first
 //    operand, so a lane holds query row (lane % 16) and keys
 //    16j + 4(lane / 16) + e of each 16-key block j.
 //  * Softmax: per-row maximum over the block (in-lane, then across the four
 //    lanes that share a row), exp2 of the score times |scale| log2(e) minus
-//    the shifted row maximum, fp32 row sums per lane.  The row shift moves
+//    the shifted row maximum.  The row sums come from the MFMA too: one
+//    more product of the fp16 probabilities with a fragment of ones leaves
+//    each row's sum in every lane of that row.  The row shift moves
 //    only when a new maximum exceeds it by more than 2^8 in probability
 //    (then the accumulators are rescaled once); probabilities up to 2^8 stay
 //    well inside fp16.
@@ -34,9 +38,8 @@
 //    ds_read_b64_tr_b16 reads of the V tile (rows = keys) give a lane 4
 //    consecutive keys of one column each, at key offsets 4(lane/16) and
 //    16 + 4(lane/16).
-//  * Epilogue: each row is divided by its sum (the four lane partials
-//    added), rounded once to fp16 or fp32, and stored; lse = |scale| *
-//    shift + ln(sum).
+//  * Epilogue: each row is divided by its sum, rounded once to fp16 or
+//    fp32, and stored; lse = |scale| * shift + ln(sum).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -73,6 +76,31 @@ struct AttnArgs {
 // distinct banks.
 __device__ inline int v_swizzle(int row) { return 2 * ((row >> 1) & 3); }
 
+// ds_read_b64_tr_b16 at a constant byte offset from `addr`, issued through
+// inline asm.  With the builtin the compiler waits for every direct-to-LDS
+// load still in flight before the read (it cannot tell that those loads
+// fill other stages), which would expose the next block's HBM latency in
+// every iteration.  Here the loop's own waits and barriers order the loads
+// and the reads, and the results are used only after lds_fence().
+template <int OFF>
+__device__ inline u32x2 ds_read_tr_asm(uint32_t addr)
+{
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+// Waits for all LDS reads issued so far, then ties each register of `v` to
+// the wait so that no use of them is scheduled before it.
+template <int N>
+__device__ inline void lds_fence(u32x2 (&v)[N])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        asm volatile("" : "+v"(v[k]));
+}
+
 __device__ inline f32x4 mfma16(const half8 &a, const half8 &b, const f32x4 &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
@@ -87,7 +115,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     constexpr int DS = kD / 32;             // d-steps of the score product
     constexpr int KS = kBN / 32;            // key steps of the P V product
     constexpr int TILE = kBN * kD;          // halves per K or V tile
-    __shared__ __attribute__((aligned(1024))) _Float16 lds[2 * 2 * TILE];
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[4 * TILE];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -119,26 +147,28 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
             qf[i][s] = __builtin_bit_cast(half8, v);
         }
 
-    // ---- K / V tiles of key block kb into LDS stage `stage` -------------
-    // One 1 KiB load of a wave fills 8 tile rows; lane l lands in physical
-    // chunk l % 8 of row l / 8 and fetches the logical chunk mapped there.
+    // ---- K / V tiles into LDS --------------------------------------------
+    // LDS holds two stages of K tiles, then two of V tiles.  The K tiles
+    // run one key block ahead of the V tiles (the scores of block kb + 1 are
+    // formed while block kb is multiplied with V).  One 1 KiB load of a wave
+    // fills 8 tile rows; lane l lands in physical chunk l % 8 of row l / 8
+    // and fetches the logical chunk the tile's swizzle maps there.
     const __amdgpu_buffer_rsrc_t rK = make_rsrc(p.K + b * Lk * kD, Lk * kD * 2);
     const __amdgpu_buffer_rsrc_t rV = make_rsrc(p.V + b * Lk * kD, Lk * kD * 2);
-    auto issue = [&](int stage, int kb) {
-        GTN_LDS _Float16 *base = (GTN_LDS _Float16 *)lds + stage * 2 * TILE;
+    auto issue_tile = [&](auto v_tag, int stage, int kb) {
+        constexpr bool IS_V = decltype(v_tag)::value;
+        GTN_LDS _Float16 *base = (GTN_LDS _Float16 *)lds +
+                                 (IS_V ? 2 * TILE : 0) + stage * TILE;
 #pragma unroll
         for (int h = 0; h < kBN / 8 / kWaves; ++h) {
             const int grp = wave + kWaves * h;
             const int row = grp * 8 + (lane >> 3);
             const uint32_t roff = (uint32_t)(kb * kBN + row) * (kD * 2);
-            const int kc = swizzle_chunk<kD>(row, lane & 7);
-            const int vc = (lane & 7) ^ v_swizzle(row);
+            const int ch = IS_V ? (lane & 7) ^ v_swizzle(row)
+                                : swizzle_chunk<kD>(row, lane & 7);
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rK, (GTN_LDS void *)(base + grp * 8 * kD), 16,
-                roff + (uint32_t)kc * 16, 0, 0, 0);
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rV, (GTN_LDS void *)(base + TILE + grp * 8 * kD), 16,
-                roff + (uint32_t)vc * 16, 0, 0, 0);
+                IS_V ? rV : rK, (GTN_LDS void *)(base + grp * 8 * kD), 16,
+                roff + (uint32_t)ch * 16, 0, 0, 0);
         }
     };
 
@@ -148,106 +178,24 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
 #pragma unroll
         for (int j = 0; j < DJ; ++j)
             oacc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float mref[MI], lsum[MI];
+    // Row sums: lacc[i] = ones * P^T accumulates, in each of its four
+    // registers, the sum of row (lane % 16) of block i.
+    f32x4 lacc[MI];
+    float mref[MI];
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         mref[i] = 0.f;
-        lsum[i] = 0.f;
+        lacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
+    const half8 ones = {1, 1, 1, 1, 1, 1, 1, 1};
 
     const int nblk = (int)((Lk + kBN - 1) / kBN);
     const int tail_keys = (int)(Lk - (int64_t)(nblk - 1) * kBN);   // 1..64
     const float c = p.c;
 
-    // Softmax of one key block, in place in sacc (scores -> probabilities),
-    // then the fp16 probability fragments of the P V product.
-    auto softmax = [&](auto tail_tag, int kb, f32x4 (&sacc)[MI][NJ],
-                       half8 (&pf)[MI][KS]) {
-        constexpr bool TAIL = decltype(tail_tag)::value;
-        float mx[MI];
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            if (TAIL) {
-#pragma unroll
-                for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (j * 16 + 4 * g + e >= tail_keys)
-                            sacc[i][j][e] = -INFINITY;
-            }
-            float m = sacc[i][0][0];
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    m = fmaxf(m, sacc[i][j][e]);
-            m = fmaxf(m, __shfl_xor(m, 16));
-            m = fmaxf(m, __shfl_xor(m, 32));
-            mx[i] = m;
-        }
-        if (kb == 0) {
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                mref[i] = mx[i];
-        } else {
-            bool need = false;
-#pragma unroll
-            for (int i = 0; i < MI; ++i)
-                need |= (mx[i] - mref[i]) * c > kLazy;
-            if (__builtin_amdgcn_ballot_w64(need) != 0) {
-#pragma unroll
-                for (int i = 0; i < MI; ++i) {
-                    const float mn = fmaxf(mref[i], mx[i]);
-                    const float f = __builtin_amdgcn_exp2f((mref[i] - mn) * c);
-                    mref[i] = mn;
-                    lsum[i] *= f;
-#pragma unroll
-                    for (int j = 0; j < DJ; ++j)
-                        oacc[i][j] *= f;
-                }
-            }
-        }
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-            const float mc = mref[i] * c;
-            float ls = 0.f;
-#pragma unroll
-            for (int j = 0; j < NJ; ++j)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    float pe = __builtin_amdgcn_exp2f(
-                        __builtin_fmaf(sacc[i][j][e], c, -mc));
-                    if (TAIL && j * 16 + 4 * g + e >= tail_keys)
-                        pe = 0.f;
-                    sacc[i][j][e] = pe;
-                    ls += pe;
-                }
-            lsum[i] += ls;
-#pragma unroll
-            for (int t = 0; t < KS; ++t) {
-                const f32x4 a = sacc[i][2 * t], bb = sacc[i][2 * t + 1];
-                pf[i][t] = half8{(_Float16)a[0], (_Float16)a[1],
-                                 (_Float16)a[2], (_Float16)a[3],
-                                 (_Float16)bb[0], (_Float16)bb[1],
-                                 (_Float16)bb[2], (_Float16)bb[3]};
-            }
-        }
-    };
-
-    issue(0, 0);
-    for (int kb = 0; kb < nblk; ++kb) {
-        const int cur = kb & 1;
-        // Own loads of block kb landed; after the barrier every wave's have,
-        // and every wave is done reading stage cur ^ 1 (block kb - 1).
-        wait_vmcnt<0>();
-        wait_lgkmcnt<0>();
-        block_sync();
-        if (kb + 1 < nblk)
-            issue(cur ^ 1, kb + 1);
-        const _Float16 *sK = lds + cur * 2 * TILE;
-        const _Float16 *sV = sK + TILE;
-
-        f32x4 sacc[MI][NJ];
+    // Scores of the key block in K stage `ks`.
+    auto score = [&](int ks, f32x4 (&sacc)[MI][NJ]) {
+        const _Float16 *sK = lds + ks * TILE;
 #pragma unroll
         for (int i = 0; i < MI; ++i)
 #pragma unroll
@@ -264,35 +212,246 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
                 for (int i = 0; i < MI; ++i)
                     sacc[i][j] = mfma16(kf, qf[i][s], sacc[i][j]);
             }
-
-        half8 pf[MI][KS];
-        if (kb == nblk - 1 && tail_keys < kBN)
-            softmax(Bool<true>{}, kb, sacc, pf);
-        else
-            softmax(Bool<false>{}, kb, sacc, pf);
-
+    };
+    // Row maxima of a block; with MASK, keys past Lk (in the last block)
+    // are set to -inf first.  A row's 64 scores sit in the four lanes
+    // l, l ^ 16, l ^ 32, l ^ 48; v_permlane32_swap / v_permlane16_swap of a
+    // value with itself bring the other half (row) of the wave alongside,
+    // so two swaps and two maxima finish the reduction in registers.
+    auto rowmax = [&](auto mask_tag, f32x4 (&sacc)[MI][NJ], float (&mx)[MI]) {
+        constexpr bool MASK = decltype(mask_tag)::value;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            if (MASK) {
+#pragma unroll
+                for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        if (j * 16 + 4 * g + e >= tail_keys)
+                            sacc[i][j][e] = -INFINITY;
+            }
+            float m = sacc[i][0][0];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    m = fmaxf(m, sacc[i][j][e]);
+            const uint32_t mu = __builtin_bit_cast(uint32_t, m);
+            const auto h32 = __builtin_amdgcn_permlane32_swap(mu, mu, false,
+                                                              false);
+            m = fmaxf(__builtin_bit_cast(float, (uint32_t)h32[0]),
+                      __builtin_bit_cast(float, (uint32_t)h32[1]));
+            const uint32_t mv = __builtin_bit_cast(uint32_t, m);
+            const auto h16 = __builtin_amdgcn_permlane16_swap(mv, mv, false,
+                                                              false);
+            mx[i] = fmaxf(__builtin_bit_cast(float, (uint32_t)h16[0]),
+                          __builtin_bit_cast(float, (uint32_t)h16[1]));
+        }
+    };
+    // The row shift: set by the first block, moved (with a rescale of the
+    // accumulators) only when a block maximum exceeds it by more than
+    // kLazy / c.
+    auto update_shift = [&](bool first, const float (&mx)[MI]) {
+        if (first) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                mref[i] = mx[i];
+            return;
+        }
+        bool need = false;
+#pragma unroll
+        for (int i = 0; i < MI; ++i)
+            need |= (mx[i] - mref[i]) * c > kLazy;
+        if (__builtin_amdgcn_ballot_w64(need) != 0) {
+#pragma unroll
+            for (int i = 0; i < MI; ++i) {
+                const float mn = fmaxf(mref[i], mx[i]);
+                const float f = __builtin_amdgcn_exp2f((mref[i] - mn) * c);
+                mref[i] = mn;
+                lacc[i] *= f;
+#pragma unroll
+                for (int j = 0; j < DJ; ++j)
+                    oacc[i][j] *= f;
+            }
+        }
+    };
+    // Probabilities of a block as the fp16 fragments of the P V product.
+    auto probs = [&](auto tail_tag, const f32x4 (&sacc)[MI][NJ],
+                     half8 (&pf)[MI][KS]) {
+        constexpr bool TAIL = decltype(tail_tag)::value;
+#pragma unroll
+        for (int i = 0; i < MI; ++i) {
+            const float mc = mref[i] * c;
+            float pr[NJ][4];
+#pragma unroll
+            for (int j = 0; j < NJ; ++j)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    float pe = __builtin_amdgcn_exp2f(
+                        __builtin_fmaf(sacc[i][j][e], c, -mc));
+                    if (TAIL && j * 16 + 4 * g + e >= tail_keys)
+                        pe = 0.f;
+                    pr[j][e] = pe;
+                }
+#pragma unroll
+            for (int t = 0; t < KS; ++t)
+                pf[i][t] = half8{
+                    (_Float16)pr[2 * t][0], (_Float16)pr[2 * t][1],
+                    (_Float16)pr[2 * t][2], (_Float16)pr[2 * t][3],
+                    (_Float16)pr[2 * t + 1][0], (_Float16)pr[2 * t + 1][1],
+                    (_Float16)pr[2 * t + 1][2], (_Float16)pr[2 * t + 1][3]};
+        }
+    };
+    // V fragments of the V tile in V stage `vs`: for column block dj and
+    // key step t, two transposing reads at key rows 32t + 16r + 4(lane/16)
+    // + (lane % 16) / 4, r = 0, 1, column 16 dj + 4 (lane % 4).  The row
+    // swizzle depends only on bits 1-2 of the row, which t and r do not
+    // change, so one address per dj serves all four reads (constant
+    // offsets of 32 and 16 rows).
+    const uint32_t lds_base = (uint32_t)(uintptr_t)(const GTN_LDS void *)lds;
+    uint32_t v_addr[DJ];
+#pragma unroll
+    for (int dj = 0; dj < DJ; ++dj) {
+        const int row = 4 * g + (r16 >> 2);
+        const int col = dj * 16 + 4 * (r16 & 3);
+        const int pc = (col >> 3) ^ v_swizzle(row);
+        v_addr[dj] = lds_base +
+                     (uint32_t)((2 * TILE + row * kD + pc * 8 + (col & 7)) * 2);
+    }
+    auto read_v = [&](int vs, u32x2 (&vr)[KS * DJ * 2]) {
+        const uint32_t so = (uint32_t)(vs * TILE * 2);
+#pragma unroll
+        for (int dj = 0; dj < DJ; ++dj) {
+            const uint32_t a = v_addr[dj] + so;
+            vr[0 * DJ * 2 + dj * 2 + 0] = ds_read_tr_asm<0>(a);
+            vr[0 * DJ * 2 + dj * 2 + 1] = ds_read_tr_asm<16 * kD * 2>(a);
+            vr[1 * DJ * 2 + dj * 2 + 0] = ds_read_tr_asm<32 * kD * 2>(a);
+            vr[1 * DJ * 2 + dj * 2 + 1] = ds_read_tr_asm<48 * kD * 2>(a);
+        }
+    };
+    static_assert(KS == 2, "two key steps per block");
+    // O += P V and the row sums, with the V fragments read by read_v.
+    auto pv = [&](u32x2 (&vr)[KS * DJ * 2], const half8 (&pf)[MI][KS]) {
+        lds_fence(vr);
 #pragma unroll
         for (int t = 0; t < KS; ++t)
 #pragma unroll
             for (int dj = 0; dj < DJ; ++dj) {
-                const int col = dj * 16 + 4 * (r16 & 3);
-                auto rd = [&](int r) {
-                    const int row = 32 * t + 16 * r + 4 * g + (r16 >> 2);
-                    const int pc = (col >> 3) ^ v_swizzle(row);
-                    const GTN_LDS _Float16 *a =
-                        (const GTN_LDS _Float16 *)sV + row * kD + pc * 8 +
-                        (col & 7);
-                    return __builtin_bit_cast(
-                        half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                   (GTN_LDS s16x4 *)a));
-                };
-                const half4 lo = rd(0), hi = rd(1);
+                const half4 lo = __builtin_bit_cast(half4, vr[t * DJ * 2 + dj * 2]);
+                const half4 hi =
+                    __builtin_bit_cast(half4, vr[t * DJ * 2 + dj * 2 + 1]);
                 const half8 vf = {lo[0], lo[1], lo[2], lo[3],
                                   hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
                     oacc[i][dj] = mfma16(vf, pf[i][t], oacc[i][dj]);
             }
+#pragma unroll
+        for (int t = 0; t < KS; ++t)
+#pragma unroll
+            for (int i = 0; i < MI; ++i)
+                lacc[i] = mfma16(ones, pf[i][t], lacc[i]);
+    };
+
+    // One pipelined step for key block kb < nblk - 1: `cur` holds its
+    // scores (shift already applied to mref), `nxt` receives the scores of
+    // block kb + 1 and their row maxima move the shift.  Two interleaved
+    // phases: the MFMAs of the next scores with the exponentials of this
+    // block, then the P V MFMAs of this block with the next row maxima.
+    // The K tile of block kb + 1 is in K stage (kb + 1) & 1 and the V tile
+    // of block kb in V stage kb & 1; the barrier orders both their arrival
+    // (each wave waited for its own loads) and the reuse of the stages read
+    // in the previous step.
+    auto step = [&](auto mask_next_tag, int kb, f32x4 (&cur)[MI][NJ],
+                    f32x4 (&nxt)[MI][NJ]) {
+        wait_vmcnt<0>();
+        wait_lgkmcnt<0>();
+        block_sync();
+        if (kb + 2 < nblk)
+            issue_tile(Bool<false>{}, kb & 1, kb + 2);
+        issue_tile(Bool<true>{}, (kb + 1) & 1, kb + 1);
+        u32x2 vr[KS * DJ * 2];
+        read_v(kb & 1, vr);
+        half8 pf[MI][KS];
+        __builtin_amdgcn_sched_barrier(0);
+        score((kb + 1) & 1, nxt);
+        probs(Bool<false>{}, cur, pf);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2 * DS * NJ / 2, 0);
+#pragma unroll
+        for (int x = 0; x < MI * NJ * DS; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 5, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        pv(vr, pf);
+        float mx[MI];
+        rowmax(mask_next_tag, nxt, mx);
+#pragma unroll
+        for (int x = 0; x < MI * (DJ + 1) * KS; ++x) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        update_shift(false, mx);
+    };
+    // The last block: no next scores.
+    auto last = [&](f32x4 (&cur)[MI][NJ]) {
+        wait_vmcnt<0>();
+        wait_lgkmcnt<0>();
+        block_sync();
+        u32x2 vr[KS * DJ * 2];
+        read_v((nblk - 1) & 1, vr);
+        half8 pf[MI][KS];
+        if (tail_keys < kBN)
+            probs(Bool<true>{}, cur, pf);
+        else
+            probs(Bool<false>{}, cur, pf);
+        pv(vr, pf);
+    };
+
+    // Prologue: K and V of block 0, K of block 1; scores and shift of
+    // block 0.
+    issue_tile(Bool<false>{}, 0, 0);
+    issue_tile(Bool<true>{}, 0, 0);
+    if (nblk > 1)
+        issue_tile(Bool<false>{}, 1, 1);
+    wait_vmcnt<0>();
+    block_sync();
+    f32x4 sa[MI][NJ], sb[MI][NJ];
+    score(0, sa);
+    {
+        float mx[MI];
+        if (nblk == 1 && tail_keys < kBN)
+            rowmax(Bool<true>{}, sa, mx);
+        else
+            rowmax(Bool<false>{}, sa, mx);
+        update_shift(true, mx);
+    }
+    // Steps 0 .. nblk - 2, unrolled by two so that the score tiles swap
+    // roles without copies; the step before the last block masks the
+    // last block's scores.
+    const bool tail = tail_keys < kBN;
+    int kb = 0;
+    for (; kb + 2 < nblk - 1; kb += 2) {
+        step(Bool<false>{}, kb, sa, sb);
+        step(Bool<false>{}, kb + 1, sb, sa);
+    }
+    if (kb + 1 < nblk - 1) {
+        // two steps left: kb (plain) and kb + 1 (before the last block)
+        step(Bool<false>{}, kb, sa, sb);
+        if (tail)
+            step(Bool<true>{}, kb + 1, sb, sa);
+        else
+            step(Bool<false>{}, kb + 1, sb, sa);
+        last(sa);
+    } else if (kb + 1 == nblk - 1) {
+        if (tail)
+            step(Bool<true>{}, kb, sa, sb);
+        else
+            step(Bool<false>{}, kb, sa, sb);
+        last(sb);
+    } else {
+        last(sa);
     }
 
     // ---- epilogue ----------------------------------------------------------
@@ -301,9 +460,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
         make_rsrc((char *)p.O + (b * Lq + q0) * kD * ES, (Lq - q0) * kD * ES);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-        float l = lsum[i];
-        l += __shfl_xor(l, 16);
-        l += __shfl_xor(l, 32);
+        const float l = lacc[i][0];
         const float inv = 1.0f / l;
 #pragma unroll
         for (int dj = 0; dj < DJ; ++dj) {

@@ -39,7 +39,8 @@
 //    consecutive keys of one column each, at key offsets 4(lane/16) and
 //    16 + 4(lane/16).
 //  * Epilogue: each row is divided by its sum, rounded once to fp16 or
-//    fp32, and stored; lse = |scale| * shift + ln(sum).
+//    fp32, and stored with the non-temporal policy (O is written once);
+//    lse = |scale| * shift + ln(sum).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -466,7 +467,16 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
         for (int dj = 0; dj < DJ; ++dj) {
             const uint32_t off =
                 (uint32_t)(((i * 16 + r16) * kD + dj * 16 + 4 * g) * ES);
-            store_out_vec4(rO, off, oacc[i][dj] * inv, (OutT *)nullptr);
+            const f32x4 o = oacc[i][dj] * inv;
+            if constexpr (ES == 2) {
+                const half4 h = {(_Float16)o[0], (_Float16)o[1],
+                                 (_Float16)o[2], (_Float16)o[3]};
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    __builtin_bit_cast(u32x2, h), rO, off, 0, GTN_STORE_CPOL);
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, o), rO, off, 0, GTN_STORE_CPOL);
+            }
         }
         const int64_t row = q0 + i * 16 + r16;
         if (p.lse != nullptr && g == 0 && row < Lq)

@@ -93,6 +93,32 @@ bool vector_outputs(bool d_aligned16, bool c_aligned16, int64_t N,
             (c_aligned16 && (ld.c * es) % 16 == 0 && (sC * es) % 16 == 0));
 }
 
+// The tile kernel (and, for split-K, the reduction) over the problem in a:
+// `splits` slices of a.k_split, `grid` workgroups.
+int launch_rows(const GemmArgs &a, const Plan &p, int splits, unsigned grid,
+                bool out_f32, hipStream_t s)
+{
+    const bool split = splits > 1;
+    hipError_t e;
+    switch (p.tile) {
+    case TILE_256:
+        e = launch_tile256(a, p.loader, p.layout, out_f32, split, p.vec_out,
+                           grid, s);
+        break;
+    case TILE_128:
+        e = launch_tile128(a, p.loader, p.layout, out_f32, split, p.vec_out,
+                           grid, s);
+        break;
+    default:
+        e = launch_tile64(a, p.loader, p.layout, out_f32, split, p.vec_out,
+                          grid, s);
+        break;
+    }
+    if (e == hipSuccess && split)
+        e = launch_splitk_reduce(a, out_f32, p.vec_out, s);
+    return e == hipSuccess ? GEMM_TN_OK : GEMM_TN_ERR_LAUNCH;
+}
+
 bool layout_ok(int layout)
 {
     return layout == GEMM_TN_ROW_K || layout == GEMM_TN_ROW_MN;
@@ -155,30 +181,36 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.splits = p.splits;
     a.k_split = (int)p.k_split;
     a.group_m = p.group_m;
-    const bool split = p.splits > 1;
-    if (split) {
+    if (p.splits > 1 || p.tail_rows > 0) {
         st = get_workspace(s, p.ws_bytes, &a.ws);
         if (st != GEMM_TN_OK)
             return st;
     }
-    hipError_t e;
-    switch (p.tile) {
-    case TILE_256:
-        e = launch_tile256(a, p.loader, p.layout, out_f32, split, p.vec_out,
-                           (unsigned)p.grid, s);
-        break;
-    case TILE_128:
-        e = launch_tile128(a, p.loader, p.layout, out_f32, split, p.vec_out,
-                           (unsigned)p.grid, s);
-        break;
-    default:
-        e = launch_tile64(a, p.loader, p.layout, out_f32, split, p.vec_out,
-                          (unsigned)p.grid, s);
-        break;
-    }
-    if (e == hipSuccess && split)
-        e = launch_splitk_reduce(a, out_f32, p.vec_out, s);
-    return e == hipSuccess ? GEMM_TN_OK : GEMM_TN_ERR_LAUNCH;
+    if (p.tail_rows == 0)
+        return launch_rows(a, p, p.splits, (unsigned)p.grid, out_f32, s);
+
+    // Tail split: rows [0, m_tail) as whole tiles, rows [m_tail, M) as a
+    // split-K problem of their own (operand A, C and D start at row m_tail
+    // of every batch entry; the batch strides stay).
+    const int64_t m_tail = (int64_t)(p.tiles_m - p.tail_rows) * p.bm;
+    GemmArgs top = a;
+    top.M = m_tail;
+    top.tiles_m = p.tiles_m - p.tail_rows;
+    top.splits = 1;
+    top.k_split = (int)(cdiv(K, kBK) * kBK);
+    st = launch_rows(top, p, 1, (unsigned)p.grid, out_f32, s);
+    if (st != GEMM_TN_OK)
+        return st;
+    GemmArgs bot = a;
+    bot.A = ld.a_mn ? a.A + m_tail : a.A + m_tail * lda;
+    bot.C = C ? (const char *)C + m_tail * ldc * es : nullptr;
+    bot.D = (char *)D + m_tail * ldd * es;
+    bot.M = M - m_tail;
+    bot.tiles_m = p.tail_rows;
+    bot.splits = p.tail_splits;
+    bot.k_split = (int)p.tail_k_split;
+    return launch_rows(bot, p, p.tail_splits, (unsigned)p.tail_grid, out_f32,
+                       s);
 }
 
 }  // namespace

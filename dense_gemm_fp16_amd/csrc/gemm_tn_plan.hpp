@@ -31,6 +31,9 @@ constexpr int kTileDirectLays[NUM_TILES] = {
     GTN_T256_DIRECT_LAYS, GTN_T128_DIRECT_LAYS, GTN_T64_DIRECT_LAYS};
 constexpr bool kTileElemLays[NUM_TILES] = {
     GTN_T256_ELEM_LAYS, GTN_T128_ELEM_LAYS, GTN_T64_ELEM_LAYS};
+// Workgroups of each tile that fit on one CU at once (LDS-limited: the 256
+// tile's rings take 160 KiB, the others 64 KiB of the 160 KiB).
+constexpr int kTileWgsPerCu[NUM_TILES] = {1, 2, 2};
 constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
 
@@ -61,6 +64,14 @@ struct Plan {
     int64_t grid = 0;
     int64_t ws_ld = 0;
     int64_t ws_bytes = 0;
+    // Tail split: the last tail_rows tile rows of every batch entry run as
+    // a separate split-K problem with tail_splits slices of tail_k_split,
+    // so that a last, mostly idle wave of whole tiles becomes one wave of
+    // partial tiles; the rows above run as whole tiles (grid counts them).
+    int tail_rows = 0;
+    int tail_splits = 1;
+    int64_t tail_k_split = 0;
+    int64_t tail_grid = 0;
 };
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -152,11 +163,13 @@ inline int check_pointers(int64_t M, int64_t N, int64_t K, const void *A,
     return GEMM_TN_OK;
 }
 
-// Optional override for tuning sweeps: "tile=256|128|64,loader=0|1|2,
-// split=S,group=G" (any subset, comma separated).  Unknown keys are ignored;
+// Optional override for tuning sweeps and tests: "tile=256|128|64,
+// loader=0|1|2,split=S,group=G,tail=R,tail_split=T" (any subset, comma
+// separated; tail=0 turns the tail split off).  Unknown keys are ignored;
 // a loader that the operands' alignment does not allow is ignored.
 struct Override {
-    int tile = -1, loader = -1, split = -1, group = -1;
+    int tile = -1, loader = -1, split = -1, group = -1, tail = -1,
+        tail_split = -1;
 };
 
 inline Override parse_override(const char *s)
@@ -182,6 +195,10 @@ inline Override parse_override(const char *s)
             o.split = v >= 1 ? v : -1;
         else if (!strcmp(tok, "group"))
             o.group = v >= 1 ? v : -1;
+        else if (!strcmp(tok, "tail"))
+            o.tail = v >= 0 ? v : -1;
+        else if (!strcmp(tok, "tail_split"))
+            o.tail_split = v >= 2 ? v : -1;
     }
     return o;
 }
@@ -258,6 +275,8 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         splits = cdiv(2 * kCUs, ntiles);
     if (o.split >= 1)
         splits = o.split;
+    else if (o.tail >= 1)
+        splits = 1;      // a forced tail split replaces the whole-K split
     const int64_t max_splits = K / (4 * kBK) > 1 ? K / (4 * kBK) : 1;
     if (splits > max_splits)
         splits = max_splits;
@@ -278,14 +297,60 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (o.group >= 1)
         p.group_m = o.group;
 
-    p.grid = ntiles * p.splits;
-    if (p.grid > 0x7FFFFFFF) {
+    // Tail split.  With whole tiles only, a last wave holding less than
+    // half a wave's tiles (a wave: every CU running as many workgroups as
+    // fit) leaves most CUs idle for a whole tile's time.  Instead the
+    // fewest bottom tile rows that hold that remainder are split along K
+    // into enough slices to fill a wave (at least four k-tiles per slice),
+    // and the rows above run as whole tiles.  Chosen only for tiles that
+    // run one workgroup per CU: where two fit, the last wave's tiles run
+    // at twice the speed, and measured on 3072^3 (128 tiles) the extra
+    // launch and reduction cost more than the tail they save.
+    const int64_t row_tiles = (int64_t)p.tiles_n * batch;
+    const int64_t slots = (int64_t)kCUs * kTileWgsPerCu[tile];
+    int tail_rows = 0;
+    if (p.splits == 1) {
+        const int64_t full = ntiles / slots, rem = ntiles % slots;
+        if (kTileWgsPerCu[tile] == 1 && full >= 1 && rem > 0 &&
+            rem <= slots / 2)
+            tail_rows = (int)cdiv(rem, row_tiles);
+        if (o.tail >= 0)
+            tail_rows = o.tail;
+        if (tail_rows >= p.tiles_m)
+            tail_rows = 0;
+    }
+    if (tail_rows > 0) {
+        const int64_t tail_tiles = tail_rows * row_tiles;
+        int64_t ts = slots / tail_tiles;
+        if (o.tail_split >= 2)
+            ts = o.tail_split;
+        if (ts > max_splits)
+            ts = max_splits;
+        if (ts >= 2) {
+            p.tail_k_split = cdiv(cdiv(K, ts), kBK) * kBK;
+            ts = cdiv(K, p.tail_k_split);
+        }
+        if (ts >= 2) {
+            p.tail_rows = tail_rows;
+            p.tail_splits = (int)ts;
+            p.tail_grid = tail_tiles * ts;
+        } else {
+            p.tail_k_split = 0;
+        }
+    }
+
+    p.grid = (ntiles - (int64_t)p.tail_rows * row_tiles) * p.splits;
+    if (p.grid + p.tail_grid > 0x7FFFFFFF) {
         p.status = GEMM_TN_ERR_UNSUPPORTED;
         return p;
     }
-    if (p.splits > 1) {
+    if (p.splits > 1 || p.tail_rows > 0)
         p.ws_ld = cdiv(N, 4) * 4;
+    if (p.splits > 1)
         p.ws_bytes = (int64_t)p.splits * batch * M * p.ws_ld * 4;
+    if (p.tail_rows > 0) {
+        const int64_t tail_m = M - (int64_t)(p.tiles_m - p.tail_rows) * p.bm;
+        p.ws_bytes = (int64_t)p.tail_splits * batch * tail_m * p.ws_ld * 4;
     }
     (void)d_dtype;
     return p;
@@ -308,7 +373,8 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
     snprintf(buf, (size_t)buflen,
              "tile=%dx%dx%d stages=%d waves=%dx%d mfma=%dx%d sched=%s "
              "loader=%s a_along=%s b_along=%s split=%d k_split=%lld "
-             "vec_out=%d group_m=%d grid=%lld",
+             "vec_out=%d group_m=%d grid=%lld tail_rows=%d tail_split=%d "
+             "tail_k_split=%lld tail_grid=%lld",
              p.bm, p.bn, kTileBK[p.tile], kTileStages[p.tile],
              kTileWM[p.tile], kTileWN[p.tile], kTileMfma[p.tile],
              kTileMfma[p.tile],
@@ -317,7 +383,8 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
              loaders[p.loader], p.a_mn ? "m" : "k", p.b_mn ? "n" : "k",
              p.splits,
              (long long)p.k_split, p.vec_out ? 1 : 0, p.group_m,
-             (long long)p.grid);
+             (long long)p.grid, p.tail_rows, p.tail_splits,
+             (long long)p.tail_k_split, (long long)p.tail_grid);
     return p.status;
 }
 

@@ -36,8 +36,10 @@
  * (a hipStream_t, NULL for the default stream) and return at once; device
  * faults surface at the caller's next synchronisation.  The only memory the
  * library allocates itself is a per-(device, stream) fp32 workspace for the
- * split-K path (skinny problems with a long K); it is grown on demand and
- * kept until the process ends.
+ * split-K path (skinny problems with a long K, and the bottom tile rows of
+ * problems whose whole-tile grid would leave a mostly idle last wave: those
+ * rows are split along K while the rows above run as whole tiles); it is
+ * grown on demand and kept until the process ends.
  *
  * Errors: every entry point returns a gemm_tn_status; the library never
  * exits or aborts.  Arguments are fully validated before any HIP call, so
@@ -148,8 +150,9 @@ int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
 
 /*
  * Name of the kernel configuration gemm_tn_ex would launch for this
- * problem (tile shape, loader, split-K factor), written NUL-terminated
- * into buf (at most buflen bytes).  aligned16 != 0 means every matrix
+ * problem (tile shape, loader, split-K factor, and the tail split: the
+ * number of bottom tile rows split along K and into how many slices),
+ * written NUL-terminated into buf (at most buflen bytes).  aligned16 != 0 means every matrix
  * pointer is 16-byte aligned.  Pure host logic, no HIP call.  Returns
  * GEMM_TN_OK or the status the GEMM call would return for these sizes.
  */

@@ -150,6 +150,9 @@ WORKLOADS = {
                        scale=1.0 / math.sqrt(8192)),
     "c5_qk": dict(batch=64, M=1024, N=1024, K=64, alpha=0.125, beta=0.0,
                   out_dtype="f32", kind="normal", num=5),
+    # not one of the five: 17 x 17 tiles of 256, one wave plus a tail
+    "tail_4352": dict(batch=1, M=4352, N=4352, K=4096, alpha=1.0, beta=0.0,
+                      out_dtype="f16", kind="uniform", num=6),
 }
 
 

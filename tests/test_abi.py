@@ -209,6 +209,33 @@ def test_plans_for_the_workloads():
     assert describe(1, 0, 5, 5) == "noop"
 
 
+def test_tail_split_plans(monkeypatch):
+    # 17 x 17 tiles of 256 on 256 CUs: one wave plus 33 tiles; the last two
+    # tile rows (34 tiles) split 7 ways, the rest one wave of whole tiles
+    p = describe(1, 4352, 4352, 4096)
+    assert p["tile"].startswith("256x256x")
+    assert (p["tail_rows"], p["tail_split"], p["grid"], p["tail_grid"]) == \
+        ("2", "7", "255", "238")
+    assert int(p["tail_k_split"]) * 7 >= 4096
+    # whole waves, or a tail of more than half a wave: no tail split
+    for shape in [(1, 4096, 4096, 4096), (1, 8192, 8192, 8192),
+                  (1, 5000, 5000, 5000), (1, 1000, 1030, 1000),
+                  (64, 1024, 1024, 64), (1, 128, 4096, 8192)]:
+        assert describe(*shape)["tail_rows"] == "0", shape
+    # tiles with two workgroups per CU take no tail split by themselves
+    p = describe(1, 3072, 3072, 3072)
+    assert p["tile"].startswith("128x128x") and p["tail_rows"] == "0"
+    # too short a K for two slices of four k-tiles: no tail split
+    assert describe(1, 4352, 4352, 448)["tail_rows"] == "0"
+    monkeypatch.setenv("GEMM_TN_FORCE", "tail=0")
+    assert describe(1, 4352, 4352, 4096)["tail_rows"] == "0"
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=64,tail=2,tail_split=3")
+    p = describe(2, 600, 260, 1088)
+    assert (p["tail_rows"], p["tail_split"]) == ("2", "3")
+    assert p["grid"] == str((10 - 2) * 5 * 2)
+    assert p["tail_grid"] == str(2 * 5 * 2 * 3)
+
+
 def test_override_spec(monkeypatch):
     monkeypatch.setenv("GEMM_TN_FORCE", "tile=128,split=2,loader=0,group=2")
     p = describe(1, 512, 512, 1024)

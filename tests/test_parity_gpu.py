@@ -433,3 +433,71 @@ def test_binding_takes_transposed_views():
                  (At.transpose(1, 2), Bt.transpose(1, 2))]:
         D = g.gemm_tn(A, B, out_dtype=torch.float32)
         assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok
+
+
+TAIL_SPECS = ["tile=64,tail=2,tail_split=3", "tile=128,tail=1,tail_split=2",
+              "tile=256,tail=1,tail_split=4", "tile=64,loader=2,tail=3,tail_split=2"]
+
+
+@pytest.mark.parametrize("spec", TAIL_SPECS)
+def test_tail_split(spec, monkeypatch):
+    """The bottom tile rows as a split-K problem of their own, the rows
+    above as whole tiles: bit-exact on integer inputs, with C read, both
+    output types, a batch, operands stored along M / N and padded rows."""
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    for (batch, M, N, K, out, beta, la, lb, pad) in [
+            (2, 600, 260, 1088, "f16", 0.0, 0, 0, 0),
+            (1, 520, 200, 1152, "f32", -2.0, 1, 0, 8),
+            (3, 300, 136, 1024, "f32", 0.5, 0, 1, 16),
+            (1, 517, 133, 1031, "f32", 0.5, 1, 1, 3)]:
+        w = _int_workload(batch, M, N, K, out, alpha=0.5, beta=beta)
+        As = np.ascontiguousarray(w.A.transpose(0, 2, 1)) if la else w.A
+        Bs = np.ascontiguousarray(w.B.transpose(0, 2, 1)) if lb else w.B
+        lda, ldb, ldd = As.shape[2] + pad, Bs.shape[2] + pad, N + pad
+        dt = np.float16 if out == "f16" else np.float32
+        A = torch.from_numpy(_padded(As, lda, np.nan)).cuda()
+        B = torch.from_numpy(_padded(Bs, ldb, np.nan)).cuda()
+        C = torch.from_numpy(w.C).cuda() if w.C is not None else None
+        D = torch.from_numpy(_padded(np.zeros((batch, M, N), dt), ldd,
+                                     dt(1234.0))).cuda()
+        desc = g.describe(batch, M, N, K, beta, out, pad % 8 == 0,
+                          lds=(lda, ldb, N, ldd), layouts=(la, lb),
+                          strides=(As.shape[1] * lda, Bs.shape[1] * ldb,
+                                   M * N, M * ldd))
+        _say(f"[tail] {spec} {batch}x{M}x{N}x{K} {out} layouts {la}{lb} "
+             f"pad {pad}: {desc}")
+        assert "tail_rows=0" not in desc, desc
+        st = g.gemm_tn_ex(
+            batch, M, N, K, w.alpha, A.data_ptr(), lda, As.shape[1] * lda,
+            B.data_ptr(), ldb, Bs.shape[1] * ldb, w.beta,
+            C.data_ptr() if C is not None else None, N, M * N, D.data_ptr(),
+            ldd, M * ldd, g.GEMM_TN_F16 if out == "f16" else g.GEMM_TN_F32,
+            torch.cuda.current_stream().cuda_stream, la, lb)
+        assert st == g.OK
+        d = D.cpu().numpy()
+        assert np.all(d[:, :, N:] == dt(1234.0)), "D padding was written"
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(np.ascontiguousarray(d[:, :, :N]), ref, out)
+        assert res.ok, f"{spec} {batch}x{M}x{N}x{K}: {res}"
+
+
+def test_tail_split_chosen_by_the_planner():
+    """4352^3 leaves a tail of 33 tiles of 256 after one wave: the planner
+    splits the last two tile rows 7 ways; checked on sampled points."""
+    g = _gpu()
+    M = N = 4352
+    K = 4096
+    desc = dict(kv.split("=") for kv in g.describe(1, M, N, K, 0.0, "f32").split())
+    assert desc["tail_rows"] == "2" and desc["tail_split"] == "7", desc
+    w = _int_workload(1, M, N, K, "f32", alpha=1.0, beta=0.0)
+    _say(f"[tail] planner {M}x{N}x{K}: {desc}")
+    d = run_gpu(w)
+    pts = sample_points(1, M, N, seed=3)
+    # every row of the split tail region too
+    r = np.arange(M - 2 * 256, M, 7)
+    pts = np.concatenate([pts, np.stack([np.zeros_like(r), r, (r * 13) % N],
+                                        1)]).astype(np.int64)
+    ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
+    res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref, "f32")
+    assert res.ok, str(res)

@@ -15,7 +15,8 @@ The fp32 transpose of the pages is measured the same way with
 (8192 x 8192, 512 MiB moved: past the 256 MB last-level cache, so HBM).
 The attention forward pass O = softmax(scale Q K^T) V runs with
 `--workload attn_64x1024` (64 heads of 1024 queries and keys, d = 64: the
-score product completed into the forward pass) or `attn_small`.
+score product completed into the forward pass) or `attn_small`, and the
+fp16-accumulating GEMM with `--workload f16acc_4096`.
 """
 from __future__ import annotations
 
@@ -42,6 +43,9 @@ TRANSPOSE_SOURCES = ("transpose.hip",)
 ATTENTION_SOURCES = ("attention_fwd.hip", "gemm_tn_kernels.hpp",
                      "gemm_tn_config.hpp")
 ATTENTIONS = ("attn_64x1024", "attn_small")
+F16ACC_SOURCES = ("gemm_f16acc.hip", "gemm_tn_kernels.hpp", "gemm_tn_config.hpp")
+# fp16-accumulating GEMMs: name -> (batch, M, N, K)
+F16ACCS = {"f16acc_4096": (1, 4096, 4096, 4096)}
 # fp32 transposes: name -> (batch, M, N)
 TRANSPOSES = {"transpose_1024": (1, 1024, 1024),
               "transpose_8192": (1, 8192, 8192)}
@@ -52,6 +56,8 @@ def _sources(workload: str):
         return TRANSPOSE_SOURCES
     if workload in ATTENTIONS:
         return ATTENTION_SOURCES
+    if workload in F16ACCS:
+        return F16ACC_SOURCES
     return KERNEL_SOURCES
 
 
@@ -61,6 +67,8 @@ def _kernel_names(workload: str):
         return ("transpose_f32_kernel",)
     if workload in ATTENTIONS:
         return ("attn_fwd_kernel",)
+    if workload in F16ACCS:
+        return ("gemm_f16acc_kernel",)
     return ("gemm_tn_kernel", "splitk_reduce")
 
 
@@ -76,8 +84,8 @@ def kernel_fingerprint(workload: str = "c3_4096") -> str:
 
 
 def traffic_path(workload: str) -> str:
-    prefix = "" if workload in TRANSPOSES or workload in ATTENTIONS \
-        else "gemm_tn_"
+    prefix = "" if (workload in TRANSPOSES or workload in ATTENTIONS
+                    or workload in F16ACCS) else "gemm_tn_"
     return os.path.join(PROFILES, f"{prefix}{workload}_traffic.json")
 
 
@@ -359,6 +367,77 @@ def attention_main(a):
     print(json.dumps(line), flush=True)
 
 
+def time_f16acc(batch, M, N, K, steps, warmup):
+    """Average time of one gemm_tn_f16acc call (seconds); inputs uniform in
+    [-1, 1), drawn on the GPU (the values do not change the speed)."""
+    import torch
+    import dense_gemm_fp16_amd as g
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(0x5EED0300 + K)
+    A = (torch.rand((batch, M, K), generator=gen, device="cuda") * 2 - 1).half()
+    B = (torch.rand((batch, N, K), generator=gen, device="cuda") * 2 - 1).half()
+    D = torch.empty((batch, M, N), dtype=torch.float16, device="cuda")
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        g.gemm_tn_f16acc(A, B, out=D, stream=stream)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for _ in range(steps):
+        g.gemm_tn_f16acc(A, B, out=D, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(stop) / 1e3 / steps
+
+
+def cpu_baseline_f16acc(batch, M, N, K, target_s):
+    """The fp16-accumulating oracle (float64 numpy, one product per 16-deep
+    step) over the first R rows of D; rate scaled to TFLOP/s."""
+    from oracle import gemm_f16acc as F
+    r = np.random.default_rng(0)
+    A = r.uniform(-1, 1, (1, M, K)).astype(np.float16)
+    B = r.uniform(-1, 1, (1, N, K)).astype(np.float16)
+    rows = 16
+    while True:
+        t = time.perf_counter()
+        F.gemm_tn_f16acc(A[:, :rows], B)
+        dt = time.perf_counter() - t
+        if dt >= target_s / 4 or rows >= M:
+            break
+        rows = min(M, rows * 4)
+    return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"first {rows} of {M} rows of D ({M}x{N}x{K}), "
+                      f"{dt:.2f} s"}
+
+
+def f16acc_main(a):
+    batch, M, N, K = F16ACCS[a.workload]
+    sec = time_f16acc(batch, M, N, K, a.steps, a.warmup)
+    tflops = 2.0 * batch * M * N * K / sec / 1e12
+    t = load_traffic(a.workload)
+    line = {
+        "metric": (f"fp16-accumulating GEMM TFLOP/s at {M}x{N}x{K} (fp16 in, "
+                   f"fp16 sum every 16 k); % of MI355X fp16 MFMA peak"),
+        "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup,
+        "ms_per_step": round(sec * 1e3, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": f"tn_gemm_f16acc_{M}x{N}x{K}", "M": M, "N": N,
+                   "K": K, "batch": batch},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                     "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4),
+                     "traffic": round(t["bytes_per_launch"]) if t else None},
+    }
+    if not a.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_f16acc(batch, M, N, K,
+                                                   a.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
 def transpose_main(a):
     batch, M, N = TRANSPOSES[a.workload]
     sec = time_transpose(batch, M, N, a.steps, a.warmup)
@@ -424,6 +503,9 @@ def main():
     if a.workload in ATTENTIONS:
         attention_main(a)
         return
+    if a.workload in F16ACCS:
+        f16acc_main(a)
+        return
     w = si.workload(a.workload)
     sec = time_workload(w, a.steps, a.warmup)
     tflops = w.flops / sec / 1e12
@@ -483,6 +565,14 @@ def main():
             tf = wa.flops / s / 1e12
             gb = wa.algorithmic_bytes / s / 1e9
             print(f"{name:<14}{'attention forward, 128 queries x 64 keys':<60}"
+                  f"{s * 1e6:>10.2f}{tf:>10.1f}"
+                  f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
+                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+        for name, (batch, M, N, K) in F16ACCS.items():
+            s = time_f16acc(batch, M, N, K, a.steps, a.warmup)
+            tf = 2.0 * batch * M * N * K / s / 1e12
+            gb = 2.0 * batch * (M * K + N * K + M * N) / s / 1e9
+            print(f"{name:<14}{'fp16 accumulation, 128x128x32, k16 MFMA':<60}"
                   f"{s * 1e6:>10.2f}{tf:>10.1f}"
                   f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
                   f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)

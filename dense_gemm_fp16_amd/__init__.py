@@ -35,7 +35,7 @@ import torch  # noqa: E402,F401
 
 EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_ex",
            "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version",
-           "transpose_f32", "attention_fwd")
+           "transpose_f32", "attention_fwd", "gemm_tn_f16acc")
 
 _REBUILD = ("run `python dense_gemm_fp16_amd/build.py` "
             "(or __graft_entry__.build()) first")
@@ -69,6 +69,9 @@ _lib.transpose_f32.argtypes = [_i64, _i64, _i64, _vp, _vp, _vp]
 _lib.attention_fwd.restype = _int
 _lib.attention_fwd.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp, _vp, _vp,
                                _vp, _int, _vp, _vp]
+_lib.gemm_tn_f16acc.restype = _int
+_lib.gemm_tn_f16acc.argtypes = [_i64, _i64, _i64, _i64, _vp, _i64, _vp, _i64,
+                                _vp, _i64, _vp]
 _lib.gemm_tn_status_string.restype = ctypes.c_char_p
 _lib.gemm_tn_status_string.argtypes = [_int]
 _lib.gemm_tn_version.restype = _int
@@ -330,3 +333,47 @@ def attention_fwd_raw(batch, Lq, Lk, d, scale, q_ptr, k_ptr, v_ptr, o_ptr,
     """Raw-pointer call of attention_fwd(); returns the status code."""
     return _lib.attention_fwd(batch, Lq, Lk, d, float(scale), q_ptr, k_ptr,
                               v_ptr, o_ptr, o_dtype, lse_ptr, stream_handle)
+
+
+def gemm_tn_f16acc(A, B, out=None, stream=None):
+    """D = A @ B^T with the sum rounded to fp16 after every 16-deep step of
+    K (include/gemm_f16acc.h).  A: (M, K) or (batch, M, K), B: (N, K) or
+    (batch, N, K), contiguous float16 GPU tensors (a batch dimension made by
+    expand, stride 0, broadcasts); returns D float16 (M, N) or (batch, M,
+    N)."""
+    torch = _torch()
+    for t, n in ((A, "A"), (B, "B")):
+        if t.dtype != torch.float16 or not t.is_cuda or t.dim() not in (2, 3):
+            raise ValueError(f"{n} must be a 2-D or 3-D float16 GPU tensor")
+        if t.numel() > 0 and (t.stride(-1) != 1
+                              or t.stride(-2) != t.shape[-1]):
+            raise ValueError(f"{n} must have packed rows")
+    if A.dim() != B.dim():
+        raise ValueError("A and B need the same number of dimensions")
+    batch = A.shape[0] if A.dim() == 3 else 1
+    M, K = A.shape[-2], A.shape[-1]
+    N = B.shape[-2]
+    if B.shape[-1] != K or (A.dim() == 3 and B.shape[0] != batch):
+        raise ValueError("B must be (batch, N, K) with A's batch and K")
+    shape = (M, N) if A.dim() == 2 else (batch, M, N)
+    if out is None:
+        out = torch.empty(shape, dtype=torch.float16, device=A.device)
+    if (tuple(out.shape) != shape or out.dtype != torch.float16
+            or not out.is_contiguous() or not out.is_cuda):
+        raise ValueError(f"out must be a contiguous float16 GPU tensor of "
+                         f"shape {shape}")
+    sA = A.stride(0) if A.dim() == 3 and A.numel() > 0 else M * K
+    sB = B.stride(0) if B.dim() == 3 and B.numel() > 0 else N * K
+    st = _lib.gemm_tn_f16acc(batch, M, N, K, A.data_ptr(), sA, B.data_ptr(),
+                             sB, out.data_ptr(), M * N,
+                             _stream_handle(stream))
+    if st != OK:
+        raise GemmError(st)
+    return out
+
+
+def gemm_tn_f16acc_raw(batch, M, N, K, A_ptr, strideA, B_ptr, strideB, D_ptr,
+                       strideD, stream_handle) -> int:
+    """Raw-pointer call of gemm_tn_f16acc(); returns the status code."""
+    return _lib.gemm_tn_f16acc(batch, M, N, K, A_ptr, strideA, B_ptr, strideB,
+                               D_ptr, strideD, stream_handle)

@@ -1,5 +1,6 @@
 // fp32 matrix transpose y = x^T for gfx950 (declared in include/
-// transpose_f32.h).  One workgroup of 256 threads moves a 64 x 64 tile:
+// transpose_f32.h).  One workgroup of 256 threads moves a 64 x 64 tile
+// (tiles ordered per XCD down the columns of x, see the kernel):
 //
 //  * read: 16 consecutive lanes cover one 256-byte row segment of x with
 //    16-byte loads (4 rows per wave instruction), as the pages' row2col
@@ -46,10 +47,20 @@ transpose_f32_kernel(const float *x, float *y, int64_t M, int64_t N,
 {
     __shared__ float tile[kT * kT];
     const int t = threadIdx.x;
+    // Workgroup id -> tile.  The hardware deals consecutive ids to the 8
+    // XCDs in turn; the id is remapped so that each XCD takes a contiguous
+    // range of tiles, and tiles are walked down the columns of x (tm
+    // fastest).  Consecutive tiles of one XCD then write adjacent 256-byte
+    // pieces of the same 64 rows of y, which the memory system merges; with
+    // tn fastest those writes land 64 rows apart (measured at 8192^2: 76 us
+    // against 102 us).
     const int per_batch = tiles_m * tiles_n;
-    const int b = blockIdx.x / per_batch;
-    const int in_b = blockIdx.x - b * per_batch;
-    const int tm = in_b / tiles_n, tn = in_b - tm * tiles_n;
+    const int nwg = (int)gridDim.x, wg = (int)blockIdx.x;
+    const int xq = nwg >> 3, xr = nwg & 7, xcd = wg & 7;
+    const int logical = xcd * xq + (xcd < xr ? xcd : xr) + (wg >> 3);
+    const int b = logical / per_batch;
+    const int in_b = logical - b * per_batch;
+    const int tn = in_b / tiles_m, tm = in_b - tn * tiles_m;
     const int64_t i0 = (int64_t)tm * kT, j0 = (int64_t)tn * kT;
     const int64_t rows_left = M - i0, cols_left = N - j0;
 

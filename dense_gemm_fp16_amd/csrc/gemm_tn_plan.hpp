@@ -294,6 +294,13 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     p.layout = layout;
     p.vec_out = vec_out;
     p.group_m = tile == TILE_256 ? 4 : 8;
+    // With one or two k-tiles the operands are small next to D and the
+    // writes of D dominate: tiles in row order, so that consecutive tiles
+    // of an XCD write neighbouring pieces of the same rows (the batched
+    // 1024 x 1024 x 64 score product: 47.2 against 49.4 us with groups of
+    // 8 tile rows).
+    if (K <= 2 * kBK)
+        p.group_m = 1;
     if (o.group >= 1)
         p.group_m = o.group;
 

@@ -39,8 +39,9 @@
 //    consecutive keys of one column each, at key offsets 4(lane/16) and
 //    16 + 4(lane/16).
 //  * Epilogue: each row is divided by its sum, rounded once to fp16 or
-//    fp32, and stored with the non-temporal policy (O is written once);
-//    lse = |scale| * shift + ln(sum).
+//    fp32, staged through LDS and stored as whole rows with the
+//    non-temporal policy (O is written once); lse = |scale| * shift +
+//    ln(sum).
 #include <hip/hip_runtime.h>
 #include <math.h>
 #include <stdint.h>
@@ -116,7 +117,16 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     constexpr int DS = kD / 32;             // d-steps of the score product
     constexpr int KS = kBN / 32;            // key steps of the P V product
     constexpr int TILE = kBN * kD;          // halves per K or V tile
-    __shared__ __attribute__((aligned(1024))) _Float16 lds[4 * TILE];
+    // After the key loop the same LDS stages each wave's block of O: 32 rows
+    // padded to 144 (fp16) or 272 (fp32) bytes, so that the 16 rows a lane
+    // group writes at one column fall on distinct banks and every row
+    // starts on a 16-byte boundary.
+    constexpr int ES = OutTraits<OutT>::bytes;
+    constexpr int OROW = kD * ES + 16;                      // bytes per row
+    constexpr int OWAVE = MI * 16 * OROW;                   // bytes per wave
+    constexpr int LDS_HALVES = (4 * TILE > kWaves * OWAVE / 2)
+                                   ? 4 * TILE : kWaves * OWAVE / 2;
+    __shared__ __attribute__((aligned(1024))) _Float16 lds[LDS_HALVES];
 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -456,31 +466,45 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     }
 
     // ---- epilogue ----------------------------------------------------------
-    constexpr int ES = OutTraits<OutT>::bytes;
-    const __amdgpu_buffer_rsrc_t rO =
-        make_rsrc((char *)p.O + (b * Lq + q0) * kD * ES, (Lq - q0) * kD * ES);
+    // O / row sum, rounded once, into this wave's LDS block (every wave is
+    // done with the K and V tiles after the barrier), then read back as
+    // whole rows: each store instruction writes 8 (fp16) or 4 (fp32)
+    // complete 128- or 256-byte rows of O instead of 32-byte pieces of 16.
+    wait_lgkmcnt<0>();
+    block_sync();
+    char *ob = (char *)lds + wave * OWAVE;
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
         const float l = lacc[i][0];
         const float inv = 1.0f / l;
 #pragma unroll
         for (int dj = 0; dj < DJ; ++dj) {
-            const uint32_t off =
-                (uint32_t)(((i * 16 + r16) * kD + dj * 16 + 4 * g) * ES);
             const f32x4 o = oacc[i][dj] * inv;
+            char *dst = ob + (i * 16 + r16) * OROW + (dj * 16 + 4 * g) * ES;
             if constexpr (ES == 2) {
                 const half4 h = {(_Float16)o[0], (_Float16)o[1],
                                  (_Float16)o[2], (_Float16)o[3]};
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    __builtin_bit_cast(u32x2, h), rO, off, 0, GTN_STORE_CPOL);
+                *(u32x2 *)dst = __builtin_bit_cast(u32x2, h);
             } else {
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    __builtin_bit_cast(u32x4, o), rO, off, 0, GTN_STORE_CPOL);
+                *(f32x4 *)dst = o;
             }
         }
         const int64_t row = q0 + i * 16 + r16;
         if (p.lse != nullptr && g == 0 && row < Lq)
             p.lse[b * Lq + row] = p.scale_abs * mref[i] + logf(l);
+    }
+    wait_lgkmcnt<0>();
+    asm volatile("" ::: "memory");
+    const __amdgpu_buffer_rsrc_t rO =
+        make_rsrc((char *)p.O + (b * Lq + q0) * kD * ES, (Lq - q0) * kD * ES);
+    constexpr int LPR = kD * ES / 16;               // lanes per row
+    constexpr int RPI = 64 / LPR;                   // rows per instruction
+#pragma unroll
+    for (int it = 0; it < MI * 16 / RPI; ++it) {
+        const int row = it * RPI + lane / LPR, ch = lane % LPR;
+        const u32x4 v = *(const u32x4 *)(ob + row * OROW + ch * 16);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            v, rO, (uint32_t)(row * kD * ES + ch * 16), 0, GTN_STORE_CPOL);
     }
 }
 

@@ -501,3 +501,40 @@ def test_tail_split_chosen_by_the_planner():
     ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
     res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref, "f32")
     assert res.ok, str(res)
+
+
+@pytest.mark.parametrize("spec", ["", "tile=64,split=1"])
+def test_largest_k(spec, monkeypatch):
+    """K = 2^21, the largest supported: values in {-1, 0, 1} keep every sum
+    exact in fp32 (|sum| <= 2^21 < 2^24).  The planner splits K into many
+    slices; the forced single slice walks all 32768 k-tiles in one
+    workgroup."""
+    if spec:
+        monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    M, N, K = 16, 24, 2 ** 21
+    w = si.build("maxk", 1, M, N, K, 1.0, 0.0, "f32", "int", 0x5EED0A01)
+    w.A = (w.A.astype(np.float32) // 2).clip(-1, 1).astype(np.float16)
+    w.B = (w.B.astype(np.float32) // 2).clip(-1, 1).astype(np.float16)
+    _say(f"[max] K={K} {spec or 'planner'}: {_gpu().describe(1, M, N, K, 0.0, 'f32')}")
+    d = run_gpu(w)
+    ref = oracle.gemm_tn(w.A, w.B)
+    res = oracle.check_exact(d, ref, "f32")
+    assert res.ok, str(res)
+
+
+def test_largest_n_and_a_long_m():
+    """N = 2^20, the largest supported, and M past a million rows
+    (sampled), on integer values."""
+    w = _int_workload(1, 8, 2 ** 20, 64, "f32")
+    _say(f"[max] N={w.N}")
+    d = run_gpu(w)
+    ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+    res = oracle.check_exact(d, ref, "f32")
+    assert res.ok, str(res)
+    w = _int_workload(1, 2 ** 20 + 5, 24, 16, "f16", alpha=1.0)
+    _say(f"[max] M={w.M}")
+    d = run_gpu(w)
+    pts = sample_points(1, w.M, w.N, n_random=20000, seed=9)
+    ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
+    res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref, "f16")
+    assert res.ok, str(res)

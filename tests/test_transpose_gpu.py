@@ -69,3 +69,15 @@ def test_misaligned_pointers_take_the_element_path():
     assert ybuf[0].item() == -1.0
     assert np.array_equal(ybuf[1:].cpu().numpy().reshape(N, M),
                           T.transpose(x))
+
+
+def test_largest_supported_dimension():
+    # N = 2^23, the largest supported: x is 2 x 2^23, y is 2^23 x 2
+    import torch
+    g = _gpu()
+    x = _x((2, 2 ** 23), 77)
+    _say("[transpose] 2 x 2^23")
+    y = g.transpose_f32(torch.from_numpy(x).cuda())
+    torch.cuda.synchronize()
+    assert np.array_equal(y.cpu().numpy().view(np.uint32),
+                          T.transpose(x).view(np.uint32))

@@ -78,31 +78,6 @@ struct AttnArgs {
 // distinct banks.
 __device__ inline int v_swizzle(int row) { return 2 * ((row >> 1) & 3); }
 
-// ds_read_b64_tr_b16 at a constant byte offset from `addr`, issued through
-// inline asm.  With the builtin the compiler waits for every direct-to-LDS
-// load still in flight before the read (it cannot tell that those loads
-// fill other stages), which would expose the next block's HBM latency in
-// every iteration.  Here the loop's own waits and barriers order the loads
-// and the reads, and the results are used only after lds_fence().
-template <int OFF>
-__device__ inline u32x2 ds_read_tr_asm(uint32_t addr)
-{
-    u32x2 r;
-    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                 : "=v"(r) : "v"(addr), "n"(OFF));
-    return r;
-}
-// Waits for all LDS reads issued so far, then ties each register of `v` to
-// the wait so that no use of them is scheduled before it.
-template <int N>
-__device__ inline void lds_fence(u32x2 (&v)[N])
-{
-    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-#pragma unroll
-    for (int k = 0; k < N; ++k)
-        asm volatile("" : "+v"(v[k]));
-}
-
 __device__ inline f32x4 mfma16(const half8 &a, const half8 &b, const f32x4 &c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

@@ -165,7 +165,19 @@ struct Bool {
 template <int V>
 struct Int {
     static constexpr int value = V;
+    __device__ __host__ constexpr operator int() const { return V; }
 };
+
+// f(Int<0>{}), ..., f(Int<N - 1>{}) in order: a loop whose index is a
+// compile-time constant inside the body (an immediate offset, say).
+template <int N, int I = 0, typename F>
+__device__ inline void static_for(F &&f)
+{
+    if constexpr (I < N) {
+        f(Int<I>{});
+        static_for<N, I + 1>(static_cast<F &&>(f));
+    }
+}
 
 // s_waitcnt with only the vector-memory counter (gfx9 encoding: vmcnt in
 // bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at "no wait").
@@ -197,6 +209,42 @@ __device__ inline void block_sync()
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// ds_read_b64_tr_b16 at a constant byte offset from the LDS byte address
+// `addr`, issued through inline asm.  The compiler builtin makes the
+// compiler wait for every direct-to-LDS load still in flight before the
+// read (it cannot tell that those loads fill other stages), which exposes
+// a prefetch's whole HBM latency once per tile.  Callers order these reads
+// against the tile loads with their own waits and barriers, and use the
+// results only after an asm lgkmcnt(0) wait with the registers tied to it
+// (lds_fence): the compiler does not track the asm reads, so it inserts no
+// wait for them.
+template <int OFF>
+__device__ inline u32x2 ds_read_tr_asm(uint32_t addr)
+{
+    static_assert(OFF >= 0 && OFF < 65536, "16-bit DS offset");
+    u32x2 r;
+    asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                 : "=v"(r) : "v"(addr), "n"(OFF));
+    return r;
+}
+// Makes `v` a new value defined here, after every asm statement before
+// this one (a wait, say), so that no use of it is scheduled earlier.
+template <typename T>
+__device__ inline void tie_reg(T &v)
+{
+    asm volatile("" : "+v"(v));
+}
+// Waits for all LDS operations issued so far (as asm, which the compiler
+// neither merges nor relaxes), then ties each register of `v` to the wait.
+template <typename T, int N>
+__device__ inline void lds_fence(T (&v)[N])
+{
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int k = 0; k < N; ++k)
+        tie_reg(v[k]);
 }
 
 template <typename OutT>
@@ -581,34 +629,57 @@ gemm_tn_kernel(GemmArgs p)
     // (k, c0 + i), k = kb .. kb + 3, when lane j of the group points at
     // (kb + j / 4, c0 + 4 (j % 4)); lane group g takes k = 8g .. 8g + 7 of
     // the k-step in two such reads.
-    auto read_tr = [&](auto w_tag, const _Float16 *s, int c0, int ks) {
+    // Rows 32 ks + 8 g + 4 r + (i / 4): the swizzle reads row bits 0, 1
+    // and 3 only, which 32 ks and 4 r (bit 2 is clear below) leave alone,
+    // so one address per fragment serves both reads of every k-step, with
+    // the rest in the instruction's offset.  The reads go through asm
+    // (ds_read_tr_asm); the fragments are used after frags_ready().
+    const uint32_t lds_addr = (uint32_t)(uintptr_t)(const GTN_LDS void *)lds;
+    auto read_tr = [&](auto w_tag, int tile, int c0, auto ks_tag) {
         constexpr int W = decltype(w_tag)::value;
         constexpr int CR = W / 8;
+        constexpr int KS = decltype(ks_tag)::value;
+        static_assert(KM == 32, "k-steps of 32 rows");
         const int i = lane & 15, g = lane >> 4;
         const int col = c0 + 4 * (i & 3);
-        auto rd = [&](int r) {
-            const int row = ks * 32 + 8 * g + 4 * r + (i >> 2);
-            const int pc = swizzle_mn<CR>(row, col >> 3);
-            const GTN_LDS _Float16 *a = (const GTN_LDS _Float16 *)s +
-                                        row * W + pc * 8 + (col & 7);
-            return __builtin_bit_cast(
-                half4, __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                           (GTN_LDS s16x4 *)a));
-        };
-        const half4 lo = rd(0), hi = rd(1);
-        return half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        const int row = 8 * g + (i >> 2);
+        const uint32_t addr =
+            lds_addr + (uint32_t)((tile + row * W +
+                                   swizzle_mn<CR>(row, col >> 3) * 8 +
+                                   (col & 7)) * 2);
+        const u32x2 lo = ds_read_tr_asm<KS * 32 * W * 2>(addr);
+        const u32x2 hi = ds_read_tr_asm<(KS * 32 + 4) * W * 2>(addr);
+        return __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+    };
+    // Fragments read by ds_read_tr_asm are usable after this: a wait for
+    // all LDS reads, then the registers tied to it (no-op for TN tiles,
+    // whose plain LDS reads the compiler waits for itself).
+    auto frags_ready = [&](half8 (&af)[MI], half8 (&bf)[NI]) {
+        if constexpr (A_TR || B_TR) {
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if constexpr (A_TR) {
+#pragma unroll
+                for (int i = 0; i < MI; ++i)
+                    tie_reg(af[i]);
+            }
+            if constexpr (B_TR) {
+#pragma unroll
+                for (int j = 0; j < NI; ++j)
+                    tie_reg(bf[j]);
+            }
+        }
     };
     // Fragments are read in the order the MFMAs below consume them (B0, A0,
     // then B1.., then A1..), so the first MFMAs of a k-step depend only on
     // the oldest reads of the previous one.
-    auto read_frags2 = [&](int sta, int stb, int ks, half8 (&af)[MI],
+    auto read_frags2 = [&](int sta, int stb, auto ks, half8 (&af)[MI],
                            half8 (&bf)[NI]) {
         const _Float16 *sA = lds + a_base(sta);
         const _Float16 *sB = lds + b_base(stb);
         const int ch = ks * QN + fq;
         auto rd_a = [&](int i) {
             if constexpr (A_TR) {
-                af[i] = read_tr(Int<BM>{}, sA, wm * WTM + i * MB, ks);
+                af[i] = read_tr(Int<BM>{}, a_base(sta), wm * WTM + i * MB, ks);
             } else {
                 const int row = wm * WTM + i * MB + frow;
                 af[i] = *(const half8 *)(sA + row * BK +
@@ -617,7 +688,7 @@ gemm_tn_kernel(GemmArgs p)
         };
         auto rd_b = [&](int j) {
             if constexpr (B_TR) {
-                bf[j] = read_tr(Int<BN>{}, sB, wn * WTN + j * MB, ks);
+                bf[j] = read_tr(Int<BN>{}, b_base(stb), wn * WTN + j * MB, ks);
             } else {
                 const int row = wn * WTN + j * MB + frow;
                 bf[j] = *(const half8 *)(sB + row * BK +
@@ -633,7 +704,8 @@ gemm_tn_kernel(GemmArgs p)
         for (int i = 1; i < MI; ++i)
             rd_a(i);
     };
-    auto read_frags = [&](int stage, int ks, half8 (&af)[MI], half8 (&bf)[NI]) {
+    auto read_frags = [&](int stage, auto ks, half8 (&af)[MI],
+                          half8 (&bf)[NI]) {
         read_frags2(stage, stage, ks, af, bf);
     };
     auto mfma = [](const half8 &b, const half8 &a, const accv &c) {
@@ -703,10 +775,13 @@ gemm_tn_kernel(GemmArgs p)
                     issue_part(sa == 0 ? 2 : sa - 1,
                                k_begin + (int64_t)(kt + 2) * BK, lw, 0,
                                A_GROUPS);
+                static_for<KSTEPS>([&](auto ks) {
+                    read_frags2(sa, sb, ks, fa[ks], fb[ks]);
+                });
+                wait_lgkmcnt<0>();
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks)
-                    read_frags2(sa, sb, ks, fa[ks], fb[ks]);
-                wait_lgkmcnt<0>();
+                    frags_ready(fa[ks], fb[ks]);
                 if (grp == 1)
                     wait_vmcnt<A_GROUPS>();
                 block_sync();
@@ -739,10 +814,13 @@ gemm_tn_kernel(GemmArgs p)
             // load phase
             if (grp == 0)
                 issue_direct(cur ^ 1, k_begin + (int64_t)(kt + 1) * BK, lw);
+            static_for<KSTEPS>([&](auto ks) {
+                read_frags(cur, ks, fa[ks], fb[ks]);
+            });
+            wait_lgkmcnt<0>();
 #pragma unroll
             for (int ks = 0; ks < KSTEPS; ++ks)
-                read_frags(cur, ks, fa[ks], fb[ks]);
-            wait_lgkmcnt<0>();
+                frags_ready(fa[ks], fb[ks]);
             block_sync();
             // compute phase
             __builtin_amdgcn_s_setprio(1);
@@ -789,18 +867,19 @@ gemm_tn_kernel(GemmArgs p)
         }
         half8 fa[2][MI], fb[2][NI];
         if (ktiles > 0)
-            read_frags(0, 0, fa[0], fb[0]);
+            read_frags(0, Int<0>{}, fa[0], fb[0]);
         int cur = 0;
         for (int kt = 0; kt < ktiles; ++kt) {
             const int refill = cur == 0 ? STAGES - 1 : cur - 1;
             const int64_t k_refill = k_begin + (int64_t)(kt + STAGES - 1) * BK;
-#pragma unroll
-            for (int ks = 0; ks < KSTEPS - 1; ++ks) {
+            static_for<KSTEPS - 1>([&](auto ks) {
                 __builtin_amdgcn_sched_barrier(0);
+                frags_ready(fa[ks & 1], fb[ks & 1]);
                 if (SPREAD)
                     issue_part(refill, k_refill, wave, ks * PER,
                                (ks + 1) * PER);
-                read_frags(cur, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+                read_frags(cur, Int<decltype(ks)::value + 1>{},
+                           fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
                 mma(fa[ks & 1], fb[ks & 1]);
 #pragma unroll
                 for (int x = 0; x < MFMAS; ++x) {
@@ -811,19 +890,20 @@ gemm_tn_kernel(GemmArgs p)
                         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
                 }
                 __builtin_amdgcn_sched_barrier(0);
-            }
+            });
             constexpr int LAST = (KSTEPS - 1) & 1;
             constexpr int LAST_LOADS = SPREAD ? PER : LOADS_PER_TILE;
             const int nxt = cur + 1 == STAGES ? 0 : cur + 1;
             wait_vmcnt<WAIT_N>();
             wait_lgkmcnt<0>();
+            frags_ready(fa[LAST], fb[LAST]);
             block_sync();
             if (SPREAD)
                 issue_part(refill, k_refill, wave, (KSTEPS - 1) * PER,
                            LOADS_PER_TILE);
             else
                 issue_direct(cur, k_begin + (int64_t)(kt + STAGES) * BK, wave);
-            read_frags(nxt, 0, fa[LAST ^ 1], fb[LAST ^ 1]);
+            read_frags(nxt, Int<0>{}, fa[LAST ^ 1], fb[LAST ^ 1]);
             mma(fa[LAST], fb[LAST]);
 #pragma unroll
             for (int x = 0; x < MFMAS; ++x) {

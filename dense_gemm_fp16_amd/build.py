@@ -34,12 +34,15 @@ FLAGS = [
 ]
 
 
-# Per-file flags.  The attention kernel applies vector ALU work (the softmax,
-# the rescale by a new row maximum) to MFMA results; with the MFMA operands
-# and results in ordinary VGPRs instead of accumulation registers, none of
-# that costs a copy between the two register files.
+# Per-file flags.  The attention kernel (the softmax, the rescale by a new
+# row maximum) and the fp16-accumulating GEMM (the fp16 rounding after every
+# step) apply vector ALU work to MFMA results; with the MFMA operands and
+# results in ordinary VGPRs instead of accumulation registers, none of that
+# costs a copy between the two register files.
+_VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
 FILE_FLAGS = {
-    "attention_fwd.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"],
+    "attention_fwd.hip": _VGPR_FORM,
+    "gemm_f16acc.hip": _VGPR_FORM,
 }
 
 

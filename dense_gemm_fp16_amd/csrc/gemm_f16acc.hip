@@ -40,6 +40,8 @@ constexpr int64_t kAccMaxK = int64_t(1) << 21;
 constexpr int64_t kAccMaxN = int64_t(1) << 20;
 
 typedef _Float16 half4v __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 struct AccArgs {
     const _Float16 *A, *B;
@@ -169,10 +171,13 @@ __global__ void __launch_bounds__(kThr) gemm_f16acc_kernel(AccArgs p)
                 f32x4 a = __builtin_amdgcn_mfma_f32_16x16x16f16(bf[j], af[i],
                                                                acc[i][j], 0,
                                                                0, 0);
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    a[e] = (float)(_Float16)a[e];
-                acc[i][j] = a;
+                // rn16 of the four sums, two per packed conversion
+                const half2v lo = __builtin_convertvector(f32x2{a[0], a[1]},
+                                                          half2v);
+                const half2v hi = __builtin_convertvector(f32x2{a[2], a[3]},
+                                                          half2v);
+                acc[i][j] = f32x4{(float)lo[0], (float)lo[1], (float)hi[0],
+                                  (float)hi[1]};
             }
     };
 

@@ -127,3 +127,29 @@ def test_unaligned_operands_take_the_element_loader():
     ref = F.gemm_tn_f16acc(A[1:].reshape(M, K), B[1:].reshape(N, K))
     np.testing.assert_array_equal(d.cpu().numpy().view(np.uint16),
                                   ref.view(np.uint16))
+
+
+def test_overflow_to_infinity_stays_infinite():
+    """An fp16 accumulator that passes 65504 becomes +-inf (round to
+    nearest) and stays there, per element: row 0 overflows in the first
+    16-deep step, row 1 in the fourth (sums 19200, 38400, 57600, 76800),
+    row 2 to -inf, row 3 stays finite, and the columns of B flip signs or
+    scale.  Both the direct and the element loader run it."""
+    K = 64
+    A = np.zeros((1, 4, K), np.float16)
+    A[0, 0], A[0, 1], A[0, 2], A[0, 3] = 8192, 1200, -8192, 3
+    B = np.ones((1, 3, K), np.float16)
+    B[0, 1] = -1
+    B[0, 2] = 0.5
+    ref = F.gemm_tn_f16acc(A, B)
+    assert np.isposinf(ref[0, 0, 0]) and np.isneginf(ref[0, 0, 1])
+    assert np.isposinf(ref[0, 1, 0]) and ref[0, 1, 2] == 38400
+    assert np.isneginf(ref[0, 2, 0]) and np.all(np.isfinite(ref[0, 3]))
+    _say("[f16acc] overflow")
+    np.testing.assert_array_equal(_run(A, B).view(np.uint16),
+                                  ref.view(np.uint16))
+    # odd K: the element loader
+    A3, B3 = A[:, :, :63], B[:, :, :63]
+    ref3 = F.gemm_tn_f16acc(A3, B3)
+    np.testing.assert_array_equal(_run(A3, B3).view(np.uint16),
+                                  ref3.view(np.uint16))

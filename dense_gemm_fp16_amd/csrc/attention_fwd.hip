@@ -396,12 +396,18 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     };
 
     // Prologue: K and V of block 0, K of block 1; scores and shift of
-    // block 0.
+    // block 0.  Only Q and K of block 0 are waited for here (loads retire
+    // in issue order, so vmcnt counts the V and K tiles issued after them);
+    // the first step's wait covers the rest.
+    constexpr int TILE_LOADS = kBN / 8 / kWaves;
     issue_tile(Bool<false>{}, 0, 0);
     issue_tile(Bool<true>{}, 0, 0);
-    if (nblk > 1)
+    if (nblk > 1) {
         issue_tile(Bool<false>{}, 1, 1);
-    wait_vmcnt<0>();
+        wait_vmcnt<2 * TILE_LOADS>();
+    } else {
+        wait_vmcnt<TILE_LOADS>();
+    }
     block_sync();
     f32x4 sa[MI][NJ], sb[MI][NJ];
     score(0, sa);

@@ -167,6 +167,13 @@ def _args():
                          "--copy-calibration-mib into a traffic summary")
     ap.add_argument("--calibration-mib", type=int, default=256,
                     help="size of the calibration copy in --summarize-pmc")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time the GEMM with cold caches: a 512 MiB "
+                         "write before every launch evicts the operands "
+                         "from the L2s and the Infinity Cache")
+    ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
+                    help="median / min / max kernel time per call of "
+                         "--workload from a rocprofv3 kernel_trace.csv")
     return ap.parse_args()
 
 
@@ -198,6 +205,58 @@ def time_workload(w, steps, warmup):
     stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / 1e3 / steps
+
+
+def time_workload_cold(w, steps):
+    """Median time of one call (seconds) with cold caches: before each
+    launch a 512 MiB fill (more than the 256 MB Infinity Cache and the
+    L2s) evicts A, B and C; HIP events bracket the GEMM alone."""
+    import statistics
+    import torch
+    import dense_gemm_fp16_amd as g
+    A, B, C, D = _device_inputs(w, torch)
+    flush = torch.empty(512 * 1024 * 1024 // 4, device="cuda")
+    stream = torch.cuda.current_stream()
+    times = []
+    for i in range(steps + 1):
+        flush.fill_(float(i))
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        start.record(stream)
+        g.gemm_tn(A, B, w.alpha, w.beta, C, out=D, stream=stream)
+        stop.record(stream)
+        torch.cuda.synchronize()
+        if i:
+            times.append(start.elapsed_time(stop) / 1e3)
+    return statistics.median(times)
+
+
+def summarize_trace(csv_path, workload):
+    """Per-call kernel time of `workload` from a rocprofv3 kernel trace:
+    the kernels of one call (a split-K or tail-split call runs two or three)
+    are summed in dispatch order."""
+    import csv
+    import statistics
+    wanted = _kernel_names(workload)
+    rows = [r for r in csv.DictReader(open(csv_path))
+            if any(k in r["Kernel_Name"] for k in wanted)]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in rows]
+    names = [r["Kernel_Name"] for r in rows]
+    # a call starts with the first kernel name seen (the GEMM kernel of the
+    # first part; a reduction or a second part follows it)
+    per_call = []
+    first = names[0] if names else None
+    for n, d in zip(names, durs):
+        if n == first or not per_call:
+            per_call.append(d)
+        else:
+            per_call[-1] += d
+    ns = sorted(per_call)
+    return {"workload": workload, "calls": len(ns),
+            "kernels_per_call": len(durs) / max(len(ns), 1),
+            "median_ns": statistics.median(ns) if ns else None,
+            "min_ns": ns[0] if ns else None, "max_ns": ns[-1] if ns else None}
 
 
 def cpu_baseline(w, target_s):
@@ -472,6 +531,9 @@ def describe(w):
 
 def main():
     a = _args()
+    if a.summarize_trace:
+        print(json.dumps(summarize_trace(a.summarize_trace, a.workload)))
+        return
     if a.summarize_pmc:
         t = summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.workload,
                           a.calibration_mib)
@@ -582,6 +644,11 @@ def main():
             print(f"{name:<14}{'fp32 transpose, 64x64 tiles':<60}"
                   f"{s * 1e6:>10.2f}{'-':>10}{'-':>8}{gb:>9.0f}"
                   f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+    if a.cold:
+        cs = time_workload_cold(w, a.steps)
+        line["cold"] = {"ms_per_call": round(cs * 1e3, 5),
+                        "tflops": round(w.flops / cs / 1e12, 2),
+                        "flush_mib": 512}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -285,11 +285,18 @@ def expected_bits(ref: np.ndarray, out_dtype: str) -> np.ndarray:
 
 
 def check_exact(d: np.ndarray, ref: np.ndarray, out_dtype: str) -> Check:
-    """Bit-exact test: d must equal the correctly rounded ref."""
+    """Bit-exact test: d must equal the correctly rounded ref, except that
+    +0 and -0 match each other.  The sign of an exact zero is not part of
+    the definition: a sum whose terms cancel comes out +0 or -0 depending
+    on the order of the additions and on whether alpha (negative, say)
+    multiplies it before or after a zero beta term is added."""
     d = np.ascontiguousarray(d)
     want = expected_bits(ref, out_dtype)
     got = d.view(np.uint16 if out_dtype == "f16" else np.uint32)
-    bad = got != want
+    magnitude = np.uint16(0x7FFF) if out_dtype == "f16" else np.uint32(
+        0x7FFFFFFF)
+    both_zero = ((got & magnitude) == 0) & ((want & magnitude) == 0)
+    bad = (got != want) & ~both_zero
     n_bad = int(bad.sum())
     worst = None
     if n_bad:

@@ -299,3 +299,22 @@ def test_check_exact():
     assert not res.ok and res.worst_index == (1, 1)
     d16 = oracle.rn16_bits(ref).view(np.float16)
     assert oracle.check_exact(d16, ref, "f16").ok
+
+
+def test_check_exact_signed_zero():
+    """An exact zero matches with either sign (alpha = -2 times a sum that
+    cancels gives -0, the oracle's +0 sum plus a zero term +0); the
+    smallest subnormal of either sign does not match zero."""
+    ref = np.array([0.0, -0.0, 0.0, 1.0])
+    for out, dt, tiny in (("f16", np.float16, 2.0 ** -24),
+                          ("f32", np.float32, 2.0 ** -149)):
+        d = np.array([-0.0, 0.0, 0.0, 1.0], dt)
+        assert oracle.check_exact(d, ref, out).ok
+        for bad in (tiny, -tiny):
+            e = d.copy()
+            e[2] = dt(bad)
+            res = oracle.check_exact(e, ref, out)
+            assert not res.ok and res.n_bad == 1, (out, bad)
+        e = d.copy()
+        e[3] = dt(-1.0)
+        assert not oracle.check_exact(e, ref, out).ok

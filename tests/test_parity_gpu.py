@@ -560,3 +560,71 @@ def test_largest_n_and_a_long_m():
     ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
     res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref, "f16")
     assert res.ok, str(res)
+
+
+RANDOM_SPECS = ["", "tile=256,split=1", "tile=128,split=2", "tile=64,split=1",
+                "tile=64,split=3", "tile=128,loader=1", "tile=64,loader=2",
+                "tile=256,tail=1,tail_split=2", "tile=64,tail=1,tail_split=3"]
+
+
+def test_random_problems_bit_exact(monkeypatch):
+    """Seeded random problems through gemm_tn_ex: batch, ragged M / N / K,
+    both storages of A and B, padded row strides (padding of A, B and C
+    holds NaN, padding of D a sentinel), pointers off 16-byte alignment,
+    alpha / beta, fp16 or fp32 D and a forced kernel configuration (or the
+    planner's).  Integer inputs: bit-exact against the oracle, D's padding
+    untouched."""
+    g = _gpu()
+    r = np.random.default_rng(0x5EED0088)
+    for case in range(80):
+        batch = int(r.integers(1, 4))
+        M, N = (int(x) for x in r.integers(1, 400, 2))
+        K = int(r.integers(1, 1200))
+        la, lb = (int(x) for x in r.integers(0, 2, 2))
+        out = "f16" if r.integers(0, 2) else "f32"
+        alpha = float(r.choice([1.0, 0.5, 1.5, -2.0]))
+        beta = float(r.choice([0.0, 0.0, 0.5, -1.0]))
+        pads = [int(x) for x in r.integers(0, 17, 4)]
+        shift = [int(x) for x in r.integers(0, 2, 2)]  # elements off alignment
+        spec = str(r.choice(RANDOM_SPECS))
+        if case % 2:
+            # sizes, strides and pointers that allow 16-byte loads: the
+            # direct loader, transposing LDS reads and the tail split
+            M, N, K = (-(-x // 8) * 8 for x in (M, N, K))
+            pads = [8 * (x // 8) for x in pads]
+            shift = [0, 0]
+        monkeypatch.setenv("GEMM_TN_FORCE", spec)
+        w = _int_workload(batch, M, N, K, out, alpha=alpha, beta=beta,
+                          seed=case)
+        As = np.ascontiguousarray(w.A.transpose(0, 2, 1)) if la else w.A
+        Bs = np.ascontiguousarray(w.B.transpose(0, 2, 1)) if lb else w.B
+        lda, ldb = As.shape[2] + pads[0], Bs.shape[2] + pads[1]
+        ldc, ldd = N + pads[2], N + pads[3]
+        dt = np.float16 if out == "f16" else np.float32
+        # one element of slack in front of A and B for the shifted pointer
+        Ab = _padded(As, lda, np.nan).reshape(-1)
+        Bb = _padded(Bs, ldb, np.nan).reshape(-1)
+        A = torch.from_numpy(np.concatenate([np.full(shift[0], np.nan,
+                                                     np.float16), Ab])).cuda()
+        B = torch.from_numpy(np.concatenate([np.full(shift[1], np.nan,
+                                                     np.float16), Bb])).cuda()
+        C = (torch.from_numpy(_padded(w.C, ldc, np.nan)).cuda()
+             if w.C is not None else None)
+        D = torch.from_numpy(_padded(np.zeros((batch, M, N), dt), ldd,
+                                     dt(1234.0))).cuda()
+        _say(f"[random {case}] {spec or 'planner'} {batch}x{M}x{N}x{K} "
+             f"lay={la}{lb} out={out} a={alpha} b={beta} pads={pads} "
+             f"shift={shift}")
+        st = g.gemm_tn_ex(
+            batch, M, N, K, alpha, A.data_ptr() + 2 * shift[0], lda,
+            As.shape[1] * lda, B.data_ptr() + 2 * shift[1], ldb,
+            Bs.shape[1] * ldb, beta, C.data_ptr() if C is not None else None,
+            ldc, M * ldc, D.data_ptr(), ldd, M * ldd,
+            g.GEMM_TN_F16 if out == "f16" else g.GEMM_TN_F32,
+            torch.cuda.current_stream().cuda_stream, la, lb)
+        assert st == g.OK, (case, st)
+        d = D.cpu().numpy()
+        assert np.all(d[:, :, N:] == dt(1234.0)), f"case {case}: D padding"
+        ref = oracle.gemm_tn(w.A, w.B, alpha, beta, w.C)
+        res = oracle.check_exact(np.ascontiguousarray(d[:, :, :N]), ref, out)
+        assert res.ok, f"case {case}: {res}"

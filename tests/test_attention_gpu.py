@@ -174,3 +174,19 @@ def test_2d_inputs_and_errors():
     q128 = torch.zeros((4, 128), dtype=torch.float16, device="cuda")
     with pytest.raises(g.GemmError):
         g.attention_fwd(q128, q128, q128, 0.3)               # d = 128
+
+
+def test_random_problems_within_the_bound():
+    """Seeded random problems: batch, ragged query and key counts, scale
+    (either sign), input magnitude and output type, each within the
+    oracle's bound."""
+    r = np.random.default_rng(0x5EED0089)
+    for case in range(24):
+        batch = int(r.integers(1, 4))
+        Lq = int(r.integers(1, 300))
+        Lk = int(r.integers(1, 900))
+        scale = float(r.choice([0.125, -0.125, 0.3, 1.0, 0.05]))
+        mag = float(r.choice([0.5, 1.0, 2.0]))
+        out = "f16" if r.integers(0, 2) else "f32"
+        Q, K, V = _qkv(batch, Lq, Lk, 5000 + case, mag)
+        _check(Q, K, V, scale, out, f"random {case}")

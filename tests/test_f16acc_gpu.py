@@ -153,3 +153,21 @@ def test_overflow_to_infinity_stays_infinite():
     ref3 = F.gemm_tn_f16acc(A3, B3)
     np.testing.assert_array_equal(_run(A3, B3).view(np.uint16),
                                   ref3.view(np.uint16))
+
+
+def test_random_integer_problems_bit_exact():
+    """Seeded random shapes, batches and integer ranges (sums past 2048
+    where the fp16 roundings act): bit-exact against the oracle."""
+    r = np.random.default_rng(0x5EED008B)
+    for case in range(24):
+        batch = int(r.integers(1, 3))
+        M, N = (int(v) for v in r.integers(1, 300, 2))
+        K = int(r.integers(1, 1500))
+        if case % 2:
+            K = -(-K // 8) * 8          # rows that allow 16-byte loads
+        hi = int(r.choice([4, 8]))
+        A = _ints((batch, M, K), 8000 + case, -hi + 1, hi)
+        B = _ints((batch, N, K), 9000 + case, -hi + 1, hi)
+        _say(f"[f16acc random {case}] {(batch, M, N, K)} |x| < {hi}")
+        np.testing.assert_array_equal(_run(A, B).view(np.uint16),
+                                      F.gemm_tn_f16acc(A, B).view(np.uint16))

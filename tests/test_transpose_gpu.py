@@ -81,3 +81,22 @@ def test_largest_supported_dimension():
     torch.cuda.synchronize()
     assert np.array_equal(y.cpu().numpy().view(np.uint32),
                           T.transpose(x).view(np.uint32))
+
+
+def test_random_shapes():
+    """Seeded random shapes (half of them multiples of 4, the 16-byte
+    path): bit-exact against the oracle."""
+    import torch
+    g = _gpu()
+    r = np.random.default_rng(0x5EED008A)
+    for case in range(30):
+        batch = int(r.integers(1, 4))
+        M, N = (int(v) for v in r.integers(1, 700, 2))
+        if case % 2:
+            M, N = -(-M // 4) * 4, -(-N // 4) * 4
+        x = _x((batch, M, N), 7000 + case)
+        _say(f"[transpose random {case}] {(batch, M, N)}")
+        y = g.transpose_f32(torch.from_numpy(x).cuda())
+        ref = T.transpose(x)
+        assert np.array_equal(y.cpu().numpy().view(np.uint32),
+                              ref.view(np.uint32)), case

@@ -34,6 +34,9 @@ namespace {
 
 // Split-K workspace, one per (device, stream): calls on one stream run in
 // order, so reusing its buffer is safe; distinct streams never share one.
+// The caller holds `lock` (taken here) until its kernels are enqueued: a
+// call from another thread that grows the buffer waits for the stream
+// before freeing it, which covers only kernels already enqueued.
 struct Workspace {
     void *ptr = nullptr;
     int64_t bytes = 0;
@@ -41,12 +44,13 @@ struct Workspace {
 std::mutex g_ws_lock;
 std::map<std::pair<int, hipStream_t>, Workspace> g_ws;
 
-int get_workspace(hipStream_t s, int64_t bytes, float **out)
+int get_workspace(hipStream_t s, int64_t bytes, float **out,
+                  std::unique_lock<std::mutex> &lock)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess)
         return GEMM_TN_ERR_LAUNCH;
-    std::lock_guard<std::mutex> g(g_ws_lock);
+    lock = std::unique_lock<std::mutex>(g_ws_lock);
     Workspace &w = g_ws[std::make_pair(dev, s)];
     if (w.bytes < bytes) {
         if (w.ptr) {
@@ -181,8 +185,9 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.splits = p.splits;
     a.k_split = (int)p.k_split;
     a.group_m = p.group_m;
+    std::unique_lock<std::mutex> ws_lock;   // held until the launches
     if (p.splits > 1 || p.tail_rows > 0) {
-        st = get_workspace(s, p.ws_bytes, &a.ws);
+        st = get_workspace(s, p.ws_bytes, &a.ws, ws_lock);
         if (st != GEMM_TN_OK)
             return st;
     }

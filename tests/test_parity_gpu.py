@@ -300,6 +300,53 @@ def test_split_k_workspace_reuse(monkeypatch):
         assert res.ok, f"{batch}x{M}x{N}x{K}: {res}"
 
 
+def test_split_k_from_several_threads(monkeypatch):
+    """Host threads issuing split-K calls on one stream at once, each call
+    larger than the last (the workspace keeps growing while other threads
+    launch): every result exact.  The workspace lock is held until a call's
+    kernels are enqueued, so a growing call's wait on the stream covers
+    them before the old buffer is freed."""
+    import threading
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=64,split=4")
+    stream = torch.cuda.current_stream()
+    jobs = []
+    for t in range(4):
+        for i in range(6):
+            M = 64 + 48 * (6 * t + i)          # growing problems
+            w = _int_workload(1, M, 96, 512, "f32", seed=100 * t + i)
+            A = torch.from_numpy(w.A).cuda()
+            B = torch.from_numpy(w.B).cuda()
+            D = torch.full((1, M, 96), float("nan"), device="cuda")
+            jobs.append((t, w, A, B, D))
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker(t):
+        for (tt, w, A, B, D) in jobs:
+            if tt != t:
+                continue
+            st = g.gemm_tn_strided_batched(
+                1, w.M, w.N, w.K, 1.0, A.data_ptr(), 0, B.data_ptr(), 0,
+                0.0, None, 0, D.data_ptr(), 0, g.GEMM_TN_F32,
+                stream.cuda_stream)
+            if st != g.OK:
+                errors.append((t, st))
+
+    _say("[split threads] 4 threads x 6 growing split-K calls, one stream")
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(4)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    torch.cuda.synchronize()
+    assert not errors, errors
+    for (t, w, A, B, D) in jobs:
+        ref = oracle.gemm_tn(w.A, w.B)
+        res = oracle.check_exact(D.cpu().numpy(), ref, "f32")
+        assert res.ok, f"thread {t} M={w.M}: {res}"
+
+
 def _padded(arr, ld, fill):
     """A (batch, rows, cols) array copied into a (batch, rows, ld) buffer
     whose padding columns hold `fill`."""

@@ -203,7 +203,13 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     // are set to -inf first.  A row's 64 scores sit in the four lanes
     // l, l ^ 16, l ^ 32, l ^ 48; v_permlane32_swap / v_permlane16_swap of a
     // value with itself bring the other half (row) of the wave alongside,
-    // so two swaps and two maxima finish the reduction in registers.
+    // so two swaps and two maxima finish the reduction in registers.  The
+    // maxima are NaN-propagating (v_maximum3_f32): fmaxf's IEEE semantics
+    // would first quiet every MFMA-produced input with one more vector
+    // instruction.
+    auto vmax = [](float a, float b) {
+        return __builtin_elementwise_maximum(a, b);
+    };
     auto rowmax = [&](auto mask_tag, f32x4 (&sacc)[MI][NJ], float (&mx)[MI]) {
         constexpr bool MASK = decltype(mask_tag)::value;
 #pragma unroll
@@ -221,17 +227,17 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
             for (int j = 0; j < NJ; ++j)
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
-                    m = fmaxf(m, sacc[i][j][e]);
+                    m = vmax(m, sacc[i][j][e]);
             const uint32_t mu = __builtin_bit_cast(uint32_t, m);
             const auto h32 = __builtin_amdgcn_permlane32_swap(mu, mu, false,
                                                               false);
-            m = fmaxf(__builtin_bit_cast(float, (uint32_t)h32[0]),
-                      __builtin_bit_cast(float, (uint32_t)h32[1]));
+            m = vmax(__builtin_bit_cast(float, (uint32_t)h32[0]),
+                     __builtin_bit_cast(float, (uint32_t)h32[1]));
             const uint32_t mv = __builtin_bit_cast(uint32_t, m);
             const auto h16 = __builtin_amdgcn_permlane16_swap(mv, mv, false,
                                                               false);
-            mx[i] = fmaxf(__builtin_bit_cast(float, (uint32_t)h16[0]),
-                          __builtin_bit_cast(float, (uint32_t)h16[1]));
+            mx[i] = vmax(__builtin_bit_cast(float, (uint32_t)h16[0]),
+                         __builtin_bit_cast(float, (uint32_t)h16[1]));
         }
     };
     // The row shift: set by the first block, moved (with a rescale of the

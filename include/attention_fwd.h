@@ -35,7 +35,7 @@
  *       softmax over no keys is undefined); a non-finite scale; o_dtype
  *       not GEMM_TN_F16 / GEMM_TN_F32; NULL Q, K, V or O with work to do;
  *       size overflow; O or lse overlapping an input or each other;
- *   GEMM_TN_ERR_UNSUPPORTED : d != 64; Lk > 2^24; misaligned pointers;
+ *   GEMM_TN_ERR_UNSUPPORTED : d != 64; Lk > 2^23; misaligned pointers;
  *       more than 2^31 - 1 workgroups;
  *   GEMM_TN_ERR_LAUNCH : the HIP runtime rejected the launch.
  * batch == 0 or Lq == 0 is a no-op.

@@ -180,7 +180,9 @@ inline Override parse_override(const char *s)
     char buf[256];
     strncpy(buf, s, sizeof buf - 1);
     buf[sizeof buf - 1] = 0;
-    for (char *tok = strtok(buf, ","); tok; tok = strtok(nullptr, ",")) {
+    char *save = nullptr;   // strtok_r: calls may come from several threads
+    for (char *tok = strtok_r(buf, ",", &save); tok;
+         tok = strtok_r(nullptr, ",", &save)) {
         char *eq = strchr(tok, '=');
         if (!eq)
             continue;

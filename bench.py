@@ -72,14 +72,23 @@ def _kernel_names(workload: str):
     return ("gemm_tn_kernel", "splitk_reduce")
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines (an edit of a comment
+    does not change the kernel)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(l.rstrip() for l in text.splitlines() if l.strip())
+
+
 def kernel_fingerprint(workload: str = "c3_4096") -> str:
-    """Hash of the kernel sources; a traffic figure measured on other
-    sources does not describe the kernel being timed."""
+    """Hash of the kernel sources' code; a traffic figure measured on other
+    code does not describe the kernel being timed."""
     import hashlib
     h = hashlib.sha256()
     for f in _sources(workload):
         h.update(f.encode())
-        h.update(open(os.path.join(CSRC, f), "rb").read())
+        h.update(_code_only(open(os.path.join(CSRC, f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -7,13 +7,15 @@
 // of its A rows and B rows in kTileK-wide steps, and an inner loop walks the
 // MMA k-steps of each step).  The CDNA4 design of each stage:
 //
-//  * global -> LDS: 16-byte loads through buffer resources.  A row of a
-//    BK = 64 tile is 128 bytes = 8 chunks of 16 bytes, so 8 consecutive
-//    lanes read one full 128-byte line (coalesced).  Rows past M / N and
-//    chunks past K get an out-of-range buffer offset, which the hardware
-//    turns into zeros: that is the edge predication (page "Mat Transpose
-//    CuTe 版代码学习", chuoer47.github.io, version 1: a per-element coordinate
-//    mask decides which accesses happen).
+//  * global -> LDS: 16-byte buffer loads that write LDS directly
+//    (buffer_load_dwordx4 ... lds), no VGPR staging.  A row of a BK = 64
+//    tile is 128 bytes = 8 chunks of 16 bytes, so 8 consecutive lanes read
+//    one full 128-byte line (coalesced).  Rows past M / N and chunks past K
+//    get an out-of-range buffer offset, which the hardware turns into
+//    zeros: that is the edge predication (page "Mat Transpose CuTe 版代码学习",
+//    chuoer47.github.io, version 1: a per-element coordinate mask decides
+//    which accesses happen).  Odd sizes, strides or alignments take an
+//    element-wise loader into the same LDS layout.
 //  * LDS layout: chunk c of row r is stored at chunk c ^ f(r) of that row:
 //    an XOR swizzle of 16-byte groups, which keeps each group contiguous
 //    for 128-bit reads while spreading one logical chunk of consecutive
@@ -23,22 +25,24 @@
 //  * LDS -> registers: v_mfma_f32_16x16x32_f16 (and 32x32x16) takes, in
 //    each lane, 8 consecutive-k halves of one row of each operand; in TN
 //    storage that is one ds_read_b128 per operand per lane, with no
-//    shuffle.
+//    shuffle.  An operand stored along M / N is kept in LDS as rows of k
+//    and read with the transposing ds_read_b64_tr_b16 (swizzle_mn).
 //  * MFMA: each wave owns a (BM/WM) x (BN/WN) sub-tile as a grid of 16 x 16
-//    (or 32 x 32) fp32 accumulator blocks.  The operands are issued as (B, A), so the
-//    accumulator block is D^T: each lane then holds 4 consecutive n of one
-//    m per group of 4 registers, which the epilogue stores as one 8- or
-//    16-byte vector.
-//  * Pipeline: a ring of LDS stages; the loads of k-tile t + STAGES - 1
-//    are in flight while k-tile t is multiplied, and one barrier per k-tile
-//    orders both the read-after-write on the next stage and the
-//    write-after-read on the stage being refilled.
+//    (or 32 x 32) fp32 accumulator blocks.  The operands are issued as
+//    (B, A), so the accumulator block is D^T: each lane then holds 4
+//    consecutive n of one m per group of 4 registers.
+//  * Pipeline: the 256 x 256 tile runs 8 waves in a ping-pong schedule
+//    (two waves per SIMD, one loading while the other multiplies, A and B
+//    in separate LDS rings); the smaller tiles interleave the next k-step's
+//    fragment reads and a share of the tile loads with the MFMAs of the
+//    current k-step, with one barrier per k-tile.
 //  * Epilogue: alpha * acc (+ beta * C when beta != 0) in fp32, rounded to
-//    fp16 or fp32 with round-to-nearest-even, stored through buffer stores
-//    whose out-of-range lanes are dropped.
+//    fp16 or fp32 with round-to-nearest-even, staged through LDS and
+//    written as whole 16-byte row pieces (element stores where the rows do
+//    not allow them); out-of-range lanes are dropped.
 //  * Split-K: slices write fp32 partial tiles to a workspace; a second
 //    kernel sums them in slice order (deterministic) and applies the
-//    epilogue.
+//    epilogue.  The same path serves the bottom tile rows of a tail split.
 #pragma once
 
 #include <hip/hip_runtime.h>

@@ -268,6 +268,18 @@ def summarize_trace(csv_path, workload):
             "min_ns": ns[0] if ns else None, "max_ns": ns[-1] if ns else None}
 
 
+def _cpu_model() -> str:
+    """The host CPU's model name (/proc/cpuinfo), else the architecture."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(w, target_s):
     """The oracle on the host cores over the first R rows of D, R chosen so
     the run takes about target_s seconds; rate scaled to TFLOP/s."""
@@ -296,8 +308,8 @@ def cpu_baseline(w, target_s):
             "kind": "oracle",
             "sample": f"first {rows} of {rows_total} rows of D "
                       f"({rows}x{w.N}x{w.K}, fp64 sequential k-sum), "
-                      f"{dt:.1f} s on {threads} threads of "
-                      f"{platform.processor() or platform.machine()}"}
+                      f"{dt:.1f} s on {threads} threads of {_cpu_model()}; "
+                      f"{flops / dt / 1e9:.1f} GFLOP/s"}
 
 
 def _transpose_input(batch, M, N, torch):
@@ -348,7 +360,7 @@ def cpu_baseline_transpose(batch, M, N, target_s):
     return {"value": 8.0 * rows * N * reps / dt / 1e9, "unit": "GB/s",
             "cores": 1, "kind": "oracle",
             "sample": f"{reps} x the first {rows} of {M} rows of the "
-                      f"{M}x{N} input ({dt:.2f} s)"}
+                      f"{M}x{N} input ({dt:.2f} s on {_cpu_model()})"}
 
 
 def _attention_inputs(w, torch):
@@ -404,7 +416,8 @@ def cpu_baseline_attention(w, target_s):
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores,
             "kind": "oracle",
             "sample": f"{reps} x the first {heads} of {w.batch} heads "
-                      f"({w.Lq}x{w.Lk}x{w.d}, float64 numpy), {dt:.2f} s"}
+                      f"({w.Lq}x{w.Lk}x{w.d}, float64 numpy), {dt:.2f} s "
+                      f"on {_cpu_model()}"}
 
 
 def attention_main(a):
@@ -477,7 +490,7 @@ def cpu_baseline_f16acc(batch, M, N, K, target_s):
     return {"value": 2.0 * rows * N * K / dt / 1e12, "unit": "TFLOP/s",
             "cores": 1, "kind": "oracle",
             "sample": f"first {rows} of {M} rows of D ({M}x{N}x{K}), "
-                      f"{dt:.2f} s"}
+                      f"{dt:.2f} s on {_cpu_model()}"}
 
 
 def f16acc_main(a):

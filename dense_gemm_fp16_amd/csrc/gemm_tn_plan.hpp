@@ -310,8 +310,15 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     // half a wave's tiles (a wave: every CU running as many workgroups as
     // fit) leaves most CUs idle for a whole tile's time.  Instead the
     // fewest bottom tile rows that hold that remainder are split along K
-    // into enough slices to fill a wave (at least four k-tiles per slice),
-    // and the rows above run as whole tiles.  Chosen only for tiles that
+    // (at least four k-tiles per slice, at most a wave of workgroups), and
+    // the rows above run as whole tiles.  More slices shorten the tail's
+    // compute (about a tile's time / slices) but each adds a round trip of
+    // fp32 partials for every tail tile (written, then read by the
+    // reduction): about sqrt(9 * k-tiles / tail tiles) slices balance the
+    // two.  Measured on the 256 tile at K = 4096 (interleaved medians):
+    // 4352^2, 34 tail tiles: 142.7 / 140.7 / 141.5 / 142.7 / 146.2 us for
+    // 3 / 4 / 5 / 6 / 7 slices (the formula: 4); 6144^2, 72 tail tiles:
+    // 255.8 / 253.8 us for 2 / 3 (the formula: 3).  Chosen only for tiles that
     // run one workgroup per CU: where two fit, the last wave's tiles run
     // at twice the speed, and measured on 3072^3 (128 tiles) the extra
     // launch and reduction cost more than the tail they save.
@@ -331,6 +338,13 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (tail_rows > 0) {
         const int64_t tail_tiles = tail_rows * row_tiles;
         int64_t ts = slots / tail_tiles;
+        const int64_t ktiles = cdiv(K, kBK);
+        int64_t balance = 1;            // round(sqrt(9 * ktiles / tail_tiles))
+        while ((2 * balance + 1) * (2 * balance + 1) * tail_tiles <=
+               36 * ktiles)
+            ++balance;
+        if (balance < ts)
+            ts = balance;
         if (o.tail_split >= 2)
             ts = o.tail_split;
         if (ts > max_splits)

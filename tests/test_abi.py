@@ -211,12 +211,18 @@ def test_plans_for_the_workloads():
 
 def test_tail_split_plans(monkeypatch):
     # 17 x 17 tiles of 256 on 256 CUs: one wave plus 33 tiles; the last two
-    # tile rows (34 tiles) split 7 ways, the rest one wave of whole tiles
+    # tile rows (34 tiles) split round(sqrt(9 * 64 / 34)) = 4 ways (a wave
+    # would hold 7), the rest one wave of whole tiles
     p = describe(1, 4352, 4352, 4096)
     assert p["tile"].startswith("256x256x")
     assert (p["tail_rows"], p["tail_split"], p["grid"], p["tail_grid"]) == \
-        ("2", "7", "255", "238")
-    assert int(p["tail_k_split"]) * 7 >= 4096
+        ("2", "4", "255", "136")
+    assert int(p["tail_k_split"]) * 4 >= 4096
+    # 72 tail tiles: round(sqrt(9 * 64 / 72)) = 3, as many as a wave holds
+    p = describe(1, 6144, 6144, 4096)
+    assert (p["tail_rows"], p["tail_split"]) == ("3", "3")
+    # a longer K takes more slices: round(sqrt(9 * 128 / 34)) = 6
+    assert describe(1, 4352, 4352, 8192)["tail_split"] == "6"
     # whole waves, or a tail of more than half a wave: no tail split
     for shape in [(1, 4096, 4096, 4096), (1, 8192, 8192, 8192),
                   (1, 5000, 5000, 5000), (1, 1000, 1030, 1000),

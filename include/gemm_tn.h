@@ -45,9 +45,12 @@
  * exits or aborts.  Arguments are fully validated before any HIP call, so
  * an error return means nothing was enqueued.
  *
- * Thread safety: calls may come from several host threads.  Calls on
- * different streams that both take the split-K path use different
- * workspaces and do not race.
+ * Thread safety: calls may come from several host threads, on one stream
+ * or on several.  Calls on different streams that both take the split-K
+ * path use different workspaces and do not race; calls on one stream share
+ * its workspace in stream order (a call that must grow it waits for the
+ * stream's earlier work before freeing the old buffer, and holds the
+ * workspace until its own kernels are enqueued).
  */
 #ifndef GEMM_TN_H
 #define GEMM_TN_H

@@ -1,0 +1,91 @@
+"""bench.py's host-side helpers, on the CPU: the kernel fingerprint that
+guards the stored traffic figures, the per-call kernel-trace summary, the
+HBM-traffic summary from two counter runs, and the refusal of more than one
+GPU."""
+import csv
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+
+
+def test_code_only_drops_comments_and_blank_lines():
+    src = ("int a; // note\n\n/* block\n comment */ int b;\n"
+           "  // whole line\nint c = 1; /* x */ int d;\n")
+    assert bench._code_only(src) == "int a;\n int b;\nint c = 1;  int d;"
+    # a comment edit leaves the code, and so the fingerprint, alone
+    assert bench._code_only(src.replace("note", "other words")) == \
+        bench._code_only(src)
+    assert bench._code_only(src.replace("int c = 1", "int c = 2")) != \
+        bench._code_only(src)
+
+
+def test_fingerprints_differ_between_kernels():
+    fps = {w: bench.kernel_fingerprint(w)
+           for w in ("c3_4096", "attn_64x1024", "transpose_8192",
+                     "f16acc_4096")}
+    assert len(set(fps.values())) == 4
+    assert all(len(f) == 16 for f in fps.values())
+
+
+def _write_trace(path, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Start_Timestamp",
+                                          "End_Timestamp"])
+        w.writeheader()
+        for name, t0, t1 in rows:
+            w.writerow({"Kernel_Name": name, "Start_Timestamp": t0,
+                        "End_Timestamp": t1})
+
+
+def test_summarize_trace_sums_the_kernels_of_a_call(tmp_path):
+    gemm = "void gtn::gemm_tn_kernel<64, 64, 64, 2, 2, 4, 0, float, true>"
+    red = "void gtn::splitk_reduce_kernel<float, true>"
+    rows = [(gemm, 0, 100), (red, 100, 130), ("other_kernel", 130, 500),
+            (gemm, 1000, 1110), (red, 1110, 1140),
+            (gemm, 2000, 2090), (red, 2090, 2130)]
+    p = tmp_path / "t_kernel_trace.csv"
+    _write_trace(p, rows)
+    t = bench.summarize_trace(str(p), "c4b_skinny")
+    assert t["calls"] == 3 and t["kernels_per_call"] == 2.0
+    assert (t["min_ns"], t["median_ns"], t["max_ns"]) == (130, 130, 140)
+
+
+def _write_pmc(path, counter, rows):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name",
+                                          "Counter_Name", "Counter_Value"])
+        w.writeheader()
+        for i, (name, v) in enumerate(rows):
+            w.writerow({"Dispatch_Id": i, "Kernel_Name": name,
+                        "Counter_Name": counter, "Counter_Value": v})
+
+
+def test_summarize_pmc_scales_by_the_calibration_copy(tmp_path):
+    copy = "__amd_rocclr_copyBuffer"
+    k = "_ZN3gtn14gemm_tn_kernelILi256E"
+    fetch, write = tmp_path / "f.csv", tmp_path / "w.csv"
+    # the 256 MiB copy reads half as much as it moves in FETCH_SIZE units
+    _write_pmc(fetch, "FETCH_SIZE", [(copy, 131072.0), (k, 1000.0),
+                                     (k, 1002.0), (k, 998.0)])
+    _write_pmc(write, "WRITE_SIZE", [(copy, 262144.0), (k, 500.0),
+                                     (k, 500.0), (k, 500.0)])
+    t = bench.summarize_pmc(str(fetch), str(write), "c3_4096", 256)
+    assert t["fetch_scale"] == pytest.approx(2.0)
+    assert t["fetch_bytes"] == pytest.approx(1000.0 * 1024 * 2.0)
+    assert t["write_bytes"] == pytest.approx(500.0 * 1024)
+    assert t["bytes_per_launch"] == pytest.approx((2000.0 + 500.0) * 1024)
+    assert t["fingerprint"] == bench.kernel_fingerprint("c3_4096")
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--gpus", "2"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr

@@ -50,10 +50,9 @@
 #endif
 // Operand storages each tile has kernels for (bit L = layout L: bit 0 set
 // = A stored along M, bit 1 = B stored along N).  Direct loader: the
-// transposing LDS reads exist for 16x16 MFMA tiles; on the 256-wide tile
-// only one operand may be stored along M / N (both at once would spill).
+// transposing LDS reads exist for 16x16 MFMA tiles, every layout.
 // Element loader: every layout, except on the 256-wide tile (spills).
-#define GTN_T256_DIRECT_LAYS (GTN_T256_MFMA == 16 ? 0x7 : 0x1)
+#define GTN_T256_DIRECT_LAYS (GTN_T256_MFMA == 16 ? 0xF : 0x1)
 #define GTN_T128_DIRECT_LAYS (GTN_T128_MFMA == 16 ? 0xF : 0x1)
 #define GTN_T64_DIRECT_LAYS (GTN_T64_MFMA == 16 ? 0xF : 0x1)
 #define GTN_T256_ELEM_LAYS false

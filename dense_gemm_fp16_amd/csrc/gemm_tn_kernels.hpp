@@ -636,21 +636,27 @@ gemm_tn_kernel(GemmArgs p)
     // Rows 32 ks + 8 g + 4 r + (i / 4): the swizzle reads row bits 0, 1
     // and 3 only, which 32 ks and 4 r (bit 2 is clear below) leave alone,
     // so one address per fragment serves both reads of every k-step, with
-    // the rest in the instruction's offset.  The reads go through asm
-    // (ds_read_tr_asm); the fragments are used after frags_ready().
+    // the rest in the instruction's offset.  Fragment f of the wave's
+    // columns cbase + 16 f has byte offset ((2 cbase + 32 f) ^ 32 h) within
+    // the row (2 h the row's swizzle), and 2 cbase, 32 f and the rest of the
+    // address occupy disjoint bits, so every fragment's address is one
+    // per-lane base XOR 32 f: one register per operand instead of one per
+    // fragment.  The reads go through asm (ds_read_tr_asm); the fragments
+    // are used after frags_ready().
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(const GTN_LDS void *)lds;
-    auto read_tr = [&](auto w_tag, int tile, int c0, auto ks_tag) {
+    auto read_tr = [&](auto w_tag, int tile, int cbase, int f, auto ks_tag) {
         constexpr int W = decltype(w_tag)::value;
         constexpr int CR = W / 8;
         constexpr int KS = decltype(ks_tag)::value;
-        static_assert(KM == 32, "k-steps of 32 rows");
+        static_assert(KM == 32 && MB == 16, "k-steps of 32, 16-wide blocks");
         const int i = lane & 15, g = lane >> 4;
-        const int col = c0 + 4 * (i & 3);
         const int row = 8 * g + (i >> 2);
-        const uint32_t addr =
-            lds_addr + (uint32_t)((tile + row * W +
-                                   swizzle_mn<CR>(row, col >> 3) * 8 +
-                                   (col & 7)) * 2);
+        const uint32_t q0 =
+            (uint32_t)((2 * cbase) ^ (swizzle_mn<CR>(row, 0) * 16));
+        const uint32_t base =
+            lds_addr + (uint32_t)((tile + row * W) * 2) +
+            (uint32_t)(16 * ((i & 3) >> 1) + 8 * (i & 1)) + q0;
+        const uint32_t addr = base ^ (uint32_t)(32 * f);
         const u32x2 lo = ds_read_tr_asm<KS * 32 * W * 2>(addr);
         const u32x2 hi = ds_read_tr_asm<(KS * 32 + 4) * W * 2>(addr);
         return __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
@@ -683,7 +689,7 @@ gemm_tn_kernel(GemmArgs p)
         const int ch = ks * QN + fq;
         auto rd_a = [&](int i) {
             if constexpr (A_TR) {
-                af[i] = read_tr(Int<BM>{}, a_base(sta), wm * WTM + i * MB, ks);
+                af[i] = read_tr(Int<BM>{}, a_base(sta), wm * WTM, i, ks);
             } else {
                 const int row = wm * WTM + i * MB + frow;
                 af[i] = *(const half8 *)(sA + row * BK +
@@ -692,7 +698,7 @@ gemm_tn_kernel(GemmArgs p)
         };
         auto rd_b = [&](int j) {
             if constexpr (B_TR) {
-                bf[j] = read_tr(Int<BN>{}, b_base(stb), wn * WTN + j * MB, ks);
+                bf[j] = read_tr(Int<BN>{}, b_base(stb), wn * WTN, j, ks);
             } else {
                 const int row = wn * WTN + j * MB + frow;
                 bf[j] = *(const half8 *)(sB + row * BK +

@@ -1024,7 +1024,9 @@ gemm_tn_kernel(GemmArgs p)
         }
     };
 
-    const bool staged = SPLIT || VEC_OUT;
+    // Without 16-byte rows, beta == 0 still stages D through LDS (then one
+    // element per lane, consecutive lanes on consecutive elements of a row).
+    const bool staged = SPLIT || VEC_OUT || p.beta == 0.0f;
     if (staged) {
         // All waves are done with the pipeline's LDS (and its last loads).
         wait_vmcnt<0>();
@@ -1081,8 +1083,39 @@ gemm_tn_kernel(GemmArgs p)
         return;
     }
 
-    // Rows whose length or alignment rules out 16-byte stores: element by
-    // element, straight from the accumulators.
+    // Rows whose length or alignment rules out 16-byte stores, beta == 0:
+    // the same LDS staging, then each store instruction writes 64
+    // consecutive elements of a row (whole lines) where the accumulator
+    // layout would write 4-byte pieces 16 bytes apart in 16 rows.
+    if (!use_c) {
+        constexpr int EPR = WTN;                    // elements per staged row
+        static_assert(RPP * EPR % 64 == 0, "whole waves of elements");
+#pragma unroll
+        for (int pass = 0; pass < PASSES; ++pass) {
+            stage_pass(pass, [&](int, int, int, f32x4 v) { return v * alpha; });
+#pragma unroll
+            for (int it = 0; it < RPP * EPR / 64; ++it) {
+                const int idx = it * 64 + lane;
+                const int r = idx / EPR, ce = idx % EPR;
+                const int cb = ce * ES;               // byte column
+                const char *src = region + r * ROW_BYTES +
+                                  stage_chunk(r, cb / 16) * 16 + cb % 16;
+                const int lm = wm * WTM + pass * RPP + r;
+                const int64_t n = n0 + wn * WTN + ce;
+                const uint32_t off =
+                    n < N ? (uint32_t)((lm * ldd + n) * ES) : kOutOfRange;
+                if constexpr (ES == 4)
+                    __builtin_amdgcn_raw_buffer_store_b32(
+                        *(const uint32_t *)src, rD, off, 0, GTN_STORE_CPOL);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(
+                        *(const uint16_t *)src, rD, off, 0, GTN_STORE_CPOL);
+            }
+        }
+        return;
+    }
+
+    // With C: element by element, straight from the accumulators.
     auto store_all = [&](auto with_c) {
         constexpr bool WITH_C = decltype(with_c)::value;
 #pragma unroll

@@ -926,6 +926,12 @@ gemm_tn_kernel(GemmArgs p)
             __builtin_amdgcn_sched_barrier(0);
             cur = nxt;
         }
+        // The last iteration read k-step 0 of the tile after the last one.
+        // Nothing uses those fragments, but transposing reads are asm, which
+        // the compiler neither waits for nor keeps the registers of once
+        // their values are dead: without this wait and tie, a read still in
+        // flight could land in registers the epilogue has taken over.
+        frags_ready(fa[((KSTEPS - 1) & 1) ^ 1], fb[((KSTEPS - 1) & 1) ^ 1]);
         wait_vmcnt<0>();
     } else {
         if (ktiles > 0) {

@@ -23,44 +23,62 @@ hipError_t launch_tile64(const GemmArgs &a, int loader, int layout,
 hipError_t launch_splitk_reduce(const GemmArgs &a, bool out_f32,
                                 bool vec_out, hipStream_t s);
 
+// Kernels instantiated for a launcher: bit 0 = whole-K kernels, bit 1 =
+// split-K slices (a tile may run the two with different ring depths).
+enum { KERNELS_WHOLE = 1, KERNELS_SPLIT = 2, KERNELS_ALL = 3 };
+
 template <int BM, int BN, int BK, int WM, int WN, int ST, int MINW, int SC,
-          int MB, int LOADER, int LAY>
+          int MB, int LOADER, int LAY, int WHICH>
 void *pick_kernel(bool out_f32, bool split, bool vec_out)
 {
-    if (split)
-        return (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER, float,
-                                       true, true, MINW, SC, MB, LAY>;
-    if (out_f32)
+    if (split) {
+        if constexpr ((WHICH & KERNELS_SPLIT) != 0)
+            return (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER,
+                                           float, true, true, MINW, SC, MB,
+                                           LAY>;
+        else
+            return nullptr;
+    }
+    if constexpr ((WHICH & KERNELS_WHOLE) == 0) {
+        return nullptr;
+    } else {
+        if (out_f32)
+            return vec_out ? (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST,
+                                                     LOADER, float, false,
+                                                     true, MINW, SC, MB, LAY>
+                           : (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST,
+                                                     LOADER, float, false,
+                                                     false, MINW, SC, MB,
+                                                     LAY>;
         return vec_out ? (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST,
-                                                 LOADER, float, false, true,
-                                                 MINW, SC, MB, LAY>
+                                                 LOADER, _Float16, false,
+                                                 true, MINW, SC, MB, LAY>
                        : (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST,
-                                                 LOADER, float, false, false,
-                                                 MINW, SC, MB, LAY>;
-    return vec_out ? (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER,
-                                             _Float16, false, true, MINW, SC,
-                                             MB, LAY>
-                   : (void *)&gemm_tn_kernel<BM, BN, BK, WM, WN, ST, LOADER,
-                                             _Float16, false, false, MINW, SC,
-                                             MB, LAY>;
+                                                 LOADER, _Float16, false,
+                                                 false, MINW, SC, MB, LAY>;
+    }
 }
 
 template <int BM, int BN, int BK, int WM, int WN, int ST, int MINW, int SC,
-          int MB, int LOADER>
+          int MB, int LOADER, int WHICH>
 void *pick_layout(int layout, bool out_f32, bool split, bool vec_out)
 {
     switch (layout) {
     case 0:
-        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 0>(
+        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 0,
+                           WHICH>(
             out_f32, split, vec_out);
     case 1:
-        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 1>(
+        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 1,
+                           WHICH>(
             out_f32, split, vec_out);
     case 2:
-        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 2>(
+        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 2,
+                           WHICH>(
             out_f32, split, vec_out);
     default:
-        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 3>(
+        return pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOADER, 3,
+                           WHICH>(
             out_f32, split, vec_out);
     }
 }
@@ -72,7 +90,7 @@ void *pick_layout(int layout, bool out_f32, bool split, bool vec_out)
 // register-staged vector loader TN only.  The planner asks only for pairs
 // that exist (kTileLayouts).
 template <int BM, int BN, int BK, int WM, int WN, int ST, int MINW, int SC,
-          int MB, int DIRECT_LAYS, bool ELEM_LAYS>
+          int MB, int DIRECT_LAYS, bool ELEM_LAYS, int WHICH = KERNELS_ALL>
 hipError_t launch_tile(const GemmArgs &a, int loader, int layout, bool out_f32,
                        bool split, bool vec_out, unsigned grid, hipStream_t s)
 {
@@ -82,7 +100,7 @@ hipError_t launch_tile(const GemmArgs &a, int loader, int layout, bool out_f32,
         constexpr int L = decltype(lay_tag)::value;
         if constexpr (((DIRECT_LAYS >> L) & 1) != 0)
             fn = pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB,
-                             LOAD_DIRECT, L>(out_f32, split, vec_out);
+                             LOAD_DIRECT, L, WHICH>(out_f32, split, vec_out);
     };
     switch (loader) {
     case LOAD_DIRECT:
@@ -96,15 +114,15 @@ hipError_t launch_tile(const GemmArgs &a, int loader, int layout, bool out_f32,
     case LOAD_VREG:
         if (layout == 0)
             fn = pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOAD_VREG,
-                             0>(out_f32, split, vec_out);
+                             0, WHICH>(out_f32, split, vec_out);
         break;
     default:
         if constexpr (ELEM_LAYS)
-            fn = pick_layout<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOAD_ELEM>(
-                layout, out_f32, split, vec_out);
+            fn = pick_layout<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOAD_ELEM,
+                             WHICH>(layout, out_f32, split, vec_out);
         else if (layout == 0)
             fn = pick_kernel<BM, BN, BK, WM, WN, ST, MINW, SC, MB, LOAD_ELEM,
-                             0>(out_f32, split, vec_out);
+                             0, WHICH>(out_f32, split, vec_out);
         break;
     }
     if (fn == nullptr)

@@ -22,6 +22,9 @@ constexpr int kTileDim[NUM_TILES] = {256, 128, 64};
 constexpr int kTileBK[NUM_TILES] = {GTN_T256_BK, GTN_T128_BK, GTN_T64_BK};
 constexpr int kTileStages[NUM_TILES] = {GTN_T256_STAGES, GTN_T128_STAGES,
                                         GTN_T64_STAGES};
+// Ring depth of split-K slices (differs on the 64 tile only).
+constexpr int kTileSplitStages[NUM_TILES] = {
+    GTN_T256_STAGES, GTN_T128_STAGES, GTN_T64_SPLIT_STAGES};
 constexpr int kTileWM[NUM_TILES] = {GTN_T256_WM, 2, 2};
 constexpr int kTileWN[NUM_TILES] = {GTN_T256_WN, 2, 2};
 constexpr int kTileSched[NUM_TILES] = {GTN_T256_SCHED, 0, 0};
@@ -31,8 +34,9 @@ constexpr int kTileDirectLays[NUM_TILES] = {
     GTN_T256_DIRECT_LAYS, GTN_T128_DIRECT_LAYS, GTN_T64_DIRECT_LAYS};
 constexpr bool kTileElemLays[NUM_TILES] = {
     GTN_T256_ELEM_LAYS, GTN_T128_ELEM_LAYS, GTN_T64_ELEM_LAYS};
-// Workgroups of each tile that fit on one CU at once (LDS-limited: the 256
-// tile's rings take 160 KiB, the others 64 KiB of the 160 KiB).
+// Workgroups of each tile that fit on one CU at once, as the tail split
+// counts them (LDS-limited: the 256 tile's rings take 160 KiB, the 128
+// tile's and the 64 tile's split-K rings 64 KiB of the 160 KiB).
 constexpr int kTileWgsPerCu[NUM_TILES] = {1, 2, 2};
 constexpr int kBK = 64;   // split-K slices are multiples of every tile's BK
 constexpr int kCUs = 256;  // MI355X compute units (8 XCDs x 32)
@@ -398,7 +402,8 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
              "loader=%s a_along=%s b_along=%s split=%d k_split=%lld "
              "vec_out=%d group_m=%d grid=%lld tail_rows=%d tail_split=%d "
              "tail_k_split=%lld tail_grid=%lld",
-             p.bm, p.bn, kTileBK[p.tile], kTileStages[p.tile],
+             p.bm, p.bn, kTileBK[p.tile],
+             p.splits > 1 ? kTileSplitStages[p.tile] : kTileStages[p.tile],
              kTileWM[p.tile], kTileWN[p.tile], kTileMfma[p.tile],
              kTileMfma[p.tile],
              p.loader == PLAN_LOAD_DIRECT ? scheds[kTileSched[p.tile]]

@@ -482,13 +482,18 @@ def test_binding_takes_transposed_views():
         assert oracle.check_exact(D.cpu().numpy(), ref, "f32").ok
 
 
-@pytest.mark.parametrize("spec", ["", "tile=128,split=1"])
+@pytest.mark.parametrize("spec", ["", "tile=64,split=1", "tile=128,split=1",
+                                  "tile=256,split=1"])
 def test_stored_along_m_or_n_matches_tn_at_scale(spec, monkeypatch):
     """Float operands stored along M / N at 2048 x 1536 x 4096 (64 k-tiles,
     tile loads in flight across every k-tile's fragment reads) give the
     TN kernel's result bit for bit: every storage sums each output in the
-    same k order.  The planner's choice (256 tile for one such operand, 128
-    for both) and the 128 tile throughout."""
+    same k order.  The planner's choice and each tile forced (the 64 and
+    128 tiles run the interleaved loop, the 256 tile the ping-pong), fp16
+    and fp32 D, every call twice.  Regression: the interleaved loop's last
+    transposing reads (of a tile past the end) were left in flight into
+    registers the epilogue reused; whole wave tiles of fp16 D came out
+    wrong, differently from call to call."""
     g = _gpu()
     monkeypatch.setenv("GEMM_TN_FORCE", spec)
     gen = torch.Generator(device="cuda").manual_seed(0x5EED0077)
@@ -496,12 +501,16 @@ def test_stored_along_m_or_n_matches_tn_at_scale(spec, monkeypatch):
     A = (torch.rand(M, K, device="cuda", generator=gen) * 2 - 1).half()
     B = (torch.rand(N, K, device="cuda", generator=gen) * 2 - 1).half()
     At, Bt = A.t().contiguous(), B.t().contiguous()     # K x M, K x N
-    ref = g.gemm_tn(A, B)
-    for la, lb in [(1, 0), (0, 1), (1, 1)]:
-        _say(f"[layout at scale] {spec or 'planner'} a_mn={la} b_mn={lb}")
-        d = g.gemm_tn(At.t() if la else A, Bt.t() if lb else B)
-        torch.cuda.synchronize()
-        assert torch.equal(d, ref), (la, lb)
+    for dt in (torch.float16, torch.float32):
+        ref = g.gemm_tn(A, B, out_dtype=dt)
+        for la, lb in [(1, 0), (0, 1), (1, 1)]:
+            _say(f"[layout at scale] {spec or 'planner'} {dt} "
+                 f"a_mn={la} b_mn={lb}")
+            for _ in range(2):
+                d = g.gemm_tn(At.t() if la else A, Bt.t() if lb else B,
+                              out_dtype=dt)
+                torch.cuda.synchronize()
+                assert torch.equal(d, ref), (dt, la, lb)
 
 
 TAIL_SPECS = ["tile=64,tail=2,tail_split=3", "tile=128,tail=1,tail_split=2",

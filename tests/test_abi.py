@@ -193,12 +193,16 @@ def test_plans_for_the_workloads():
     assert p["tile"].startswith("256x256x") and p["split"] == "1"
     assert p["grid"] == "256" and p["loader"] != "elem"
     # 1024^3 and the ragged 1000x1030x1000: 64x64 tiles, enough of them
-    assert describe(1, 1024, 1024, 1024, 0.5, "f32")["tile"] == "64x64x64"
+    # (whole-K problems on the 64 tile take its two-stage ring)
+    p = describe(1, 1024, 1024, 1024, 0.5, "f32")
+    assert p["tile"] == "64x64x64" and p["stages"] == "2"
     p = describe(1, 1000, 1030, 1000, 0.0, "f32")
     assert p["tile"] == "64x64x64" and p["vec_out"] == "0"   # N % 4 != 0
-    # skinny 128x4096x8192: split-K
+    assert p["stages"] == "2"
+    # skinny 128x4096x8192: split-K, slices on the four-stage ring
     p = describe(1, 128, 4096, 8192, 0.0, "f32")
     assert int(p["split"]) > 1 and int(p["k_split"]) % 64 == 0
+    assert p["tile"] == "64x64x64" and p["stages"] == "4"
     assert int(p["split"]) * int(p["k_split"]) >= 8192
     # batched QK^T: 64 x (1024 x 1024 x 64)
     p = describe(64, 1024, 1024, 64, 0.0, "f32")

@@ -120,13 +120,7 @@ def describe(batch, M, N, K, beta=0.0, out_dtype="f16", aligned16=True,
     return buf.value.decode()
 
 
-def _torch():
-    import torch
-    return torch
-
-
 def _dtype_code(dt) -> int:
-    torch = _torch()
     if dt == torch.float16:
         return GEMM_TN_F16
     if dt == torch.float32:
@@ -134,16 +128,23 @@ def _dtype_code(dt) -> int:
     raise TypeError("C / D must be float16 or float32")
 
 
-def _stream_handle(stream):
-    torch = _torch()
-    s = stream if stream is not None else torch.cuda.current_stream()
-    return ctypes.c_void_p(s.cuda_stream)
+# The current stream's raw handle without building a Stream object (which
+# costs more than the rest of a small call's marshalling).
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+
+
+def _stream_handle(stream, t):
+    """Handle of `stream`, else of the current stream of tensor t's GPU."""
+    if stream is not None:
+        return stream.cuda_stream
+    if _raw_stream is not None:
+        return _raw_stream(t.device.index)
+    return torch.cuda.current_stream(t.device).cuda_stream
 
 
 def _operand(t, name):
     """(layout, row stride) of a 2-D operand or of each matrix of a batch:
     unit stride along K, else unit stride along M / N."""
-    torch = _torch()
     if t.dtype != torch.float16:
         raise TypeError(f"{name} must be float16")
     if not t.is_cuda:
@@ -179,7 +180,6 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
 
     `out` may be given (it is then D and is returned); otherwise D is
     allocated with `out_dtype` (default: C's dtype, else float16)."""
-    torch = _torch()
     layout_a, lda = _operand(A, "A")
     layout_b, ldb = _operand(B, "B")
     if A.dim() != B.dim() or A.dim() not in (2, 3):
@@ -217,7 +217,7 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
         batch, M, N, K, float(alpha), A.data_ptr(), layout_a, lda,
         _bstride(A), B.data_ptr(), layout_b, ldb, _bstride(B), float(beta),
         c_ptr, ldc, sc, out.data_ptr(), _ld(out), _bstride(out), code,
-        _stream_handle(stream))
+        _stream_handle(stream, out))
     if st != OK:
         raise GemmError(st)
     return out
@@ -254,7 +254,6 @@ def gemm_tn_ex(batch, M, N, K, alpha, A_ptr, lda, strideA, B_ptr, ldb,
 def transpose_f32(x, out=None, stream=None):
     """y = x^T for a contiguous float32 (M, N) or (batch, M, N) GPU tensor
     (include/transpose_f32.h); returns y of shape (N, M) or (batch, N, M)."""
-    torch = _torch()
     if x.dtype != torch.float32 or not x.is_cuda or not x.is_contiguous():
         raise ValueError("x must be a contiguous float32 GPU tensor")
     if x.dim() not in (2, 3):
@@ -269,7 +268,7 @@ def transpose_f32(x, out=None, stream=None):
         raise ValueError(f"out must be a contiguous float32 GPU tensor "
                          f"of shape {shape}")
     st = _lib.transpose_f32(batch, M, N, x.data_ptr(), out.data_ptr(),
-                            _stream_handle(stream))
+                            _stream_handle(stream, out))
     if st != OK:
         raise GemmError(st)
     return out
@@ -290,7 +289,6 @@ def attention_fwd(q, k, v, scale: float, out=None, out_dtype=None,
     a float32 `lse` tensor of shape (batch, Lq) / (Lq,)), the natural
     log-sum-exp of each row of scale * q k^T is written too and (O, lse) is
     returned; otherwise O."""
-    torch = _torch()
     for t, n in ((q, "q"), (k, "k"), (v, "v")):
         if (t.dtype != torch.float16 or not t.is_cuda
                 or not t.is_contiguous() or t.dim() not in (2, 3)):
@@ -322,7 +320,7 @@ def attention_fwd(q, k, v, scale: float, out=None, out_dtype=None,
                             k.data_ptr(), v.data_ptr(), out.data_ptr(),
                             _dtype_code(out.dtype),
                             lse.data_ptr() if lse is not None else None,
-                            _stream_handle(stream))
+                            _stream_handle(stream, out))
     if st != OK:
         raise GemmError(st)
     return (out, lse) if lse is not None else out
@@ -341,7 +339,6 @@ def gemm_tn_f16acc(A, B, out=None, stream=None):
     (batch, N, K), contiguous float16 GPU tensors (a batch dimension made by
     expand, stride 0, broadcasts); returns D float16 (M, N) or (batch, M,
     N)."""
-    torch = _torch()
     for t, n in ((A, "A"), (B, "B")):
         if t.dtype != torch.float16 or not t.is_cuda or t.dim() not in (2, 3):
             raise ValueError(f"{n} must be a 2-D or 3-D float16 GPU tensor")
@@ -366,7 +363,7 @@ def gemm_tn_f16acc(A, B, out=None, stream=None):
     sB = B.stride(0) if B.dim() == 3 and B.numel() > 0 else N * K
     st = _lib.gemm_tn_f16acc(batch, M, N, K, A.data_ptr(), sA, B.data_ptr(),
                              sB, out.data_ptr(), M * N,
-                             _stream_handle(stream))
+                             _stream_handle(stream, out))
     if st != OK:
         raise GemmError(st)
     return out

@@ -39,21 +39,61 @@ _lib = None
 C_F16, C_F32 = 0, 1
 
 
+# Planted mistakes (a CPU-only device for testing the pins): number ->
+# (what it models, [(text of gemm_oracle.c, replacement)]).  A mutant copy
+# of the source is written next to the build and compiled under its own
+# name; the oracle's own source holds no trace of them.
+MUTANTS = {
+    1: ("last k term dropped",
+        [("for (int64_t k = 0; k < K; ++k)",
+          "for (int64_t k = 0; k < K - (K > 0); ++k)")]),
+    2: ("B read as K x N",
+        [("const double *brow = job->b + (bi * job->N + j) * job->K;",
+          "const double *brow = job->b + bi * job->N * job->K + j;"),
+         ("int64_t bstep = 1;", "int64_t bstep = job->N;")]),
+    3: ("sign of the beta term",
+        [("r = r + beta * load_c(C, c_dtype, cidx);",
+          "r = r - beta * load_c(C, c_dtype, cidx);")]),
+    4: ("fp16 subnormals flushed",
+        [("v = ldexp((double)m, -24);", "v = 0.0;")]),
+    5: ("encode truncates",
+        [("if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0))",
+          "if (0)")]),
+    6: ("batch index of B ignored",
+        [("int64_t bi = r / job->M;", "int64_t bi = 0;")]),
+}
+
+
+def _mutant_source(n: int) -> str:
+    text = open(_SRC).read()
+    for old, new in MUTANTS[n][1]:
+        if text.count(old) != 1:
+            raise RuntimeError(f"mutant {n}: {old!r} not found once")
+        text = text.replace(old, new)
+    path = os.path.join(_HERE, "_mutant%d.c" % n)
+    with open(path, "w") as f:
+        f.write(text)
+    return path
+
+
 def build(force: bool = True, mutant: int = 0) -> str:
     """Compile the oracle with gcc (no fused multiply-add, no fast-math).
 
-    `mutant` > 0 builds a copy with a planted mistake (see ORACLE_MUTANT in
-    gemm_oracle.c) under a separate name; the tests use those copies to
-    show that the pins reject each mistake."""
+    `mutant` > 0 builds a copy with planted mistake number `mutant` (see
+    MUTANTS) under a separate name; the tests use those copies to show that
+    the pins reject each mistake."""
     path = _LIB_PATH if mutant == 0 else os.path.join(
         _HERE, "libgemm_oracle_mutant%d.so" % mutant)
     if force or not os.path.exists(path):
+        src = _SRC if mutant == 0 else _mutant_source(mutant)
         tmp = path + ".tmp%d" % os.getpid()
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-D_GNU_SOURCE", "-ffp-contract=off",
-             "-fno-fast-math", "-fPIC", "-shared", "-pthread",
-             "-DORACLE_MUTANT=%d" % mutant, "-o", tmp, _SRC, "-lm"])
+             "-fno-fast-math", "-fPIC", "-shared", "-pthread", "-o", tmp, src,
+             "-lm"])
         os.replace(tmp, path)
+        if src != _SRC:
+            os.remove(src)
     return path
 
 
@@ -285,18 +325,16 @@ def expected_bits(ref: np.ndarray, out_dtype: str) -> np.ndarray:
 
 
 def check_exact(d: np.ndarray, ref: np.ndarray, out_dtype: str) -> Check:
-    """Bit-exact test: d must equal the correctly rounded ref, except that
-    +0 and -0 match each other.  The sign of an exact zero is not part of
-    the definition: a sum whose terms cancel comes out +0 or -0 depending
-    on the order of the additions and on whether alpha (negative, say)
-    multiplies it before or after a zero beta term is added."""
+    """Bit-exact test: d must equal the correctly rounded ref, bit for bit,
+    the sign of a zero included.  For integer-valued inputs that sign is
+    unique: under IEEE 754 round-to-nearest, x + (-x) is +0 and +0 + (-0) is
+    +0, so a sum that starts at +0 and whose exact value is 0 ends at +0 in
+    any order of the additions; alpha * (+0) and the beta term then follow
+    the same sign rules on both sides."""
     d = np.ascontiguousarray(d)
     want = expected_bits(ref, out_dtype)
     got = d.view(np.uint16 if out_dtype == "f16" else np.uint32)
-    magnitude = np.uint16(0x7FFF) if out_dtype == "f16" else np.uint32(
-        0x7FFFFFFF)
-    both_zero = ((got & magnitude) == 0) & ((want & magnitude) == 0)
-    bad = (got != want) & ~both_zero
+    bad = got != want
     n_bad = int(bad.sum())
     worst = None
     if n_bad:

@@ -240,10 +240,9 @@ def test_pin(pin):
     pin()
 
 
-# mutant number -> the mistake planted (gemm_oracle.c, ORACLE_MUTANT)
-MUTANTS = {1: "last k term dropped", 2: "B read as K x N",
-           3: "sign of the beta term", 4: "fp16 subnormals flushed",
-           5: "encode truncates", 6: "batch index of B ignored"}
+# mutant number -> the mistake planted (oracle.MUTANTS: text substitutions
+# applied to a copy of gemm_oracle.c)
+MUTANTS = {n: what for n, (what, _) in oracle.MUTANTS.items()}
 
 
 @pytest.mark.parametrize("n", sorted(MUTANTS), ids=list(MUTANTS.values()))
@@ -302,14 +301,22 @@ def test_check_exact():
 
 
 def test_check_exact_signed_zero():
-    """An exact zero matches with either sign (alpha = -2 times a sum that
-    cancels gives -0, the oracle's +0 sum plus a zero term +0); the
-    smallest subnormal of either sign does not match zero."""
+    """The sign of an exact zero is part of the bit-exact check: the
+    oracle's +0 sum times alpha = -2 is -0, and a +0 there fails; the
+    smallest subnormal of either sign does not match zero either."""
+    ref = oracle.gemm_tn(np.array([[1.0, 1.0]], np.float16),
+                         np.array([[1.0, -1.0]], np.float16), alpha=-2.0)
+    assert ref[0, 0] == 0.0 and np.signbit(ref[0, 0])       # -2 * (+0)
     ref = np.array([0.0, -0.0, 0.0, 1.0])
     for out, dt, tiny in (("f16", np.float16, 2.0 ** -24),
                           ("f32", np.float32, 2.0 ** -149)):
-        d = np.array([-0.0, 0.0, 0.0, 1.0], dt)
+        d = np.array([0.0, -0.0, 0.0, 1.0], dt)
         assert oracle.check_exact(d, ref, out).ok
+        for k, z in ((0, -0.0), (1, 0.0)):
+            e = d.copy()
+            e[k] = dt(z)
+            res = oracle.check_exact(e, ref, out)
+            assert not res.ok and res.n_bad == 1, (out, k)
         for bad in (tiny, -tiny):
             e = d.copy()
             e[2] = dt(bad)
@@ -318,3 +325,21 @@ def test_check_exact_signed_zero():
         e = d.copy()
         e[3] = dt(-1.0)
         assert not oracle.check_exact(e, ref, out).ok
+
+
+def test_oracle_zero_sums_are_positive():
+    """IEEE round-to-nearest: a sum that starts at +0 and cancels exactly,
+    or whose terms are all zeros of either sign, is +0 (so the sign of a
+    zero result is alpha's, unless the beta term decides it)."""
+    A = np.array([[0.0, 0.0, 0.0], [3.0, -1.0, -2.0], [-0.0, -0.0, -0.0]],
+                 np.float16)
+    B = np.array([[-1.0, -2.0, 3.0], [1.0, 1.0, 1.0]], np.float16)
+    ref = oracle.gemm_tn(A, B)
+    zero = ref == 0.0
+    assert zero.sum() == 5 and not np.signbit(ref[zero]).any()
+    neg = oracle.gemm_tn(A, B, alpha=-0.5)
+    assert np.signbit(neg[zero]).all()
+    C = np.full((3, 2), -0.0, np.float32)
+    # +0 + beta * (-0): +0 for beta > 0; -0 + (-0) = -0 for negative alpha
+    assert not np.signbit(oracle.gemm_tn(A, B, 1.0, 1.0, C)[zero]).any()
+    assert np.signbit(oracle.gemm_tn(A, B, -1.0, 1.0, C)[zero]).all()

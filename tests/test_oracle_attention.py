@@ -242,3 +242,50 @@ def test_bound_rejects_planted_mistakes():
     assert AT.check(O_drop, None, Q, K, V, 0.125, "f32")["O_fail"] > 0
     O_base, _ = AT.attention(Q, K, V, 0.125 / math.log(2.0))
     assert AT.check(O_base, None, Q, K, V, 0.125, "f32")["O_fail"] > 0
+
+
+SPACING = os.path.join(os.path.dirname(__file__), "golden",
+                       "fp16_half_spacing.json")
+
+
+@pytest.mark.parametrize("case", json.load(open(SPACING))["cases"],
+                         ids=lambda c: c[0])
+def test_half_ulp_f16_golden(case):
+    """half_ulp_f16 against half-spacings worked by hand from the binary16
+    definition, including values that round up across a binade boundary
+    and the subnormal range, where the spacing stays 2^-24."""
+    _, x, _, half = case
+    assert AT.half_ulp_f16(np.array([x]))[0] == half
+    assert AT.half_ulp_f16(np.array([-x]))[0] == half
+
+
+def test_half_ulp_f16_matches_the_gemm_oracle_codec():
+    """Across every finite binade (and below the normal range) the
+    attention oracle's half spacing equals half of the GEMM oracle's ulp16
+    taken at its own RNE encoding (both pinned separately: that codec
+    against all 65536 patterns).  Values that round to infinity have no
+    spacing and are left out."""
+    import oracle
+    r = np.random.default_rng(0x5EED0300)
+    x = np.ldexp(r.uniform(1.0, 2.0, 20000), r.integers(-30, 16, 20000))
+    x = np.concatenate([x, np.ldexp(1.0, np.arange(-30, 16)),
+                        np.ldexp(1.0, np.arange(-30, 16)) * (1 - 2.0 ** -12)])
+    x = x[x < 65520.0]
+    x = np.where(r.integers(0, 2, x.size) == 1, -x, x)
+    want = 0.5 * oracle.ulp16(oracle.decode_f16(oracle.rn16_bits(x)))
+    np.testing.assert_array_equal(AT.half_ulp_f16(x), want)
+
+
+def test_half_ulp_f16_pin_catches_an_exponent_off_by_one():
+    """A half spacing one binade too large or too small (the kind of slip
+    the formula invites) fails the golden table."""
+    cases = json.load(open(SPACING))["cases"]
+    x = np.array([c[1] for c in cases])
+    want = np.array([c[3] for c in cases])
+    good = AT.half_ulp_f16(x)
+    assert np.array_equal(good, want)
+    for wrong in (good * 2, good / 2):
+        assert not np.array_equal(wrong, want)
+    # the spacing at x instead of at rn16(x): misses the binade crossings
+    e = np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -14)))
+    assert not np.array_equal(0.5 * 2.0 ** (e - 10), want)

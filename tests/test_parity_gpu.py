@@ -63,53 +63,53 @@ def sample_points(batch, M, N, n_random=4000, seed=0):
     return np.concatenate(pts).astype(np.int64)
 
 
-FULL = ["c1_256", "c2_1024", "c4a_ragged", "c4b_skinny"]
-SAMPLED = ["c3_4096", "c5_qk"]
+WORKLOADS = ["c1_256", "c2_1024", "c3_4096", "c4a_ragged", "c4b_skinny",
+             "c5_qk"]
 
 
-@pytest.mark.parametrize("name", FULL + SAMPLED)
+def full_check(w, d, exact):
+    """Every element of d against the oracle, in blocks of at most 1024
+    flattened rows (the 4096^3 and 64-batch results would otherwise hold
+    several GiB of float64 temporaries).  Returns the first failing block's
+    result, or the last block's."""
+    flat = d.reshape(w.batch * w.M, w.N)
+    step = 1024
+    res = None
+    for r0 in range(0, w.batch * w.M, step):
+        r1 = min(r0 + step, w.batch * w.M)
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C, rows=(r0, r1))
+        res = (oracle.check_exact(flat[r0:r1], ref, w.out_dtype) if exact
+               else oracle.check(flat[r0:r1], ref, w.K, w.out_dtype))
+        if not res.ok:
+            res.worst_index = (r0 + res.worst_index[0],) + tuple(
+                res.worst_index[1:])
+            return res
+    return res
+
+
+@pytest.mark.parametrize("name", WORKLOADS)
 def test_workload_tolerance(name):
+    """Every element of every workload, at its full size, within the
+    tolerance."""
     w = si.workload(name)
     _say(f"[parity] {name} {w.batch}x{w.M}x{w.N}x{w.K} out={w.out_dtype}")
     d = run_gpu(w)
     assert np.isfinite(d.astype(np.float64)).all()
-    if name in FULL:
-        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
-        res = oracle.check(d, ref, w.K, w.out_dtype)
-    else:
-        pts = sample_points(w.batch, w.M, w.N)
-        ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
-        got = d[pts[:, 0], pts[:, 1], pts[:, 2]]
-        res = oracle.check(got, ref, w.K, w.out_dtype)
+    res = full_check(w, d, exact=False)
     _say(f"[parity] {name}: {res}")
     assert res.ok, str(res)
 
 
-@pytest.mark.parametrize("name", FULL + SAMPLED)
+@pytest.mark.parametrize("name", WORKLOADS)
 def test_workload_integer_bit_exact(name):
+    """Every element of every workload's integer-valued variant, at its full
+    size, bit for bit."""
     w = si.workload(name, int_values=True)
     _say(f"[exact] {name} {w.batch}x{w.M}x{w.N}x{w.K} out={w.out_dtype}")
     d = run_gpu(w)
-    if name in FULL:
-        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
-        res = oracle.check_exact(d, ref, w.out_dtype)
-    else:
-        pts = sample_points(w.batch, w.M, w.N, seed=1)
-        ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
-        res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref,
-                                 w.out_dtype)
+    res = full_check(w, d, exact=True)
     _say(f"[exact] {name}: {res}")
     assert res.ok, str(res)
-
-
-def test_c5_full_batches():
-    # every element of a few whole batches of the attention-score product
-    w = si.workload("c5_qk")
-    d = run_gpu(w)
-    for b in (0, 17, 63):
-        ref = oracle.gemm_tn(w.A[b], w.B[b], w.alpha)
-        res = oracle.check(d[b], ref, w.K, w.out_dtype)
-        assert res.ok, f"batch {b}: {res}"
 
 
 EDGE = [1, 2, 7, 8, 9, 31, 32, 33, 63, 64, 65, 127, 129, 255, 257]
@@ -562,7 +562,7 @@ def test_tail_split(spec, monkeypatch):
 
 def test_tail_split_chosen_by_the_planner():
     """4352^3 leaves a tail of 33 tiles of 256 after one wave: the planner
-    splits the last two tile rows 4 ways; checked on sampled points."""
+    splits the last two tile rows 4 ways; every element checked."""
     g = _gpu()
     M = N = 4352
     K = 4096
@@ -571,13 +571,7 @@ def test_tail_split_chosen_by_the_planner():
     w = _int_workload(1, M, N, K, "f32", alpha=1.0, beta=0.0)
     _say(f"[tail] planner {M}x{N}x{K}: {desc}")
     d = run_gpu(w)
-    pts = sample_points(1, M, N, seed=3)
-    # every row of the split tail region too
-    r = np.arange(M - 2 * 256, M, 7)
-    pts = np.concatenate([pts, np.stack([np.zeros_like(r), r, (r * 13) % N],
-                                        1)]).astype(np.int64)
-    ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
-    res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref, "f32")
+    res = full_check(w, d, exact=True)
     assert res.ok, str(res)
 
 
@@ -612,9 +606,7 @@ def test_largest_n_and_a_long_m():
     w = _int_workload(1, 2 ** 20 + 5, 24, 16, "f16", alpha=1.0)
     _say(f"[max] M={w.M}")
     d = run_gpu(w)
-    pts = sample_points(1, w.M, w.N, n_random=20000, seed=9)
-    ref = oracle.gemm_tn_points(w.A, w.B, pts, w.alpha, w.beta, w.C)
-    res = oracle.check_exact(d[pts[:, 0], pts[:, 1], pts[:, 2]], ref, "f16")
+    res = full_check(w, d, exact=True)
     assert res.ok, str(res)
 
 
@@ -684,3 +676,63 @@ def test_random_problems_bit_exact(monkeypatch):
         ref = oracle.gemm_tn(w.A, w.B, alpha, beta, w.C)
         res = oracle.check_exact(np.ascontiguousarray(d[:, :, :N]), ref, out)
         assert res.ok, f"case {case}: {res}"
+
+
+def _signed_zero_problem(out):
+    """Integer problem whose outputs include exact-zero sums formed every
+    way the kernels can form them: all-zero products of either sign, a
+    multi-term cancellation inside one MFMA k-step, and cancellations
+    across k-steps, across k-tiles and across split-K slices (+260 then
+    -260 over K = 520); C holds zeros of both signs."""
+    r = np.random.default_rng(0x5EED0A55)
+    M, N, K = 96, 80, 520
+    A = r.integers(-3, 4, (M, K)).astype(np.float16)
+    B = r.integers(-3, 4, (N, K)).astype(np.float16)
+    A[0] = 0.0
+    A[1] = np.float16(-0.0)
+    A[2] = 1.0
+    B[0] = -1.0
+    B[1, :260], B[1, 260:] = 1.0, -1.0          # slices / k-tiles
+    B[2] = 0.0
+    B[2, 0], B[2, 1:4] = 3.0, -1.0              # inside one k-step
+    B[3] = 0.0
+    B[3, 5], B[3, 40] = 2.0, -2.0               # across k-steps
+    B[4] = 0.0
+    B[4, 10], B[4, 500] = 1.0, -1.0             # across k-tiles
+    B[5] = np.float16(-0.0)
+    dt = np.float16 if out == "f16" else np.float32
+    C = r.integers(-3, 4, (M, N)).astype(dt)
+    C[(C == 0) & (r.integers(0, 2, (M, N)) == 1)] = dt(-0.0)
+    return A, B, C
+
+
+SIGNED_ZERO_SPECS = ["", "tile=256,tail=1,tail_split=2",
+                     "tile=64,tail=1,tail_split=3"] + CONFIGS
+
+
+@pytest.mark.parametrize("spec", SIGNED_ZERO_SPECS)
+def test_signed_zero_bit_exact(spec, monkeypatch):
+    """The sign of every exact zero matches the oracle bit for bit on every
+    kernel configuration (tile, loader, split-K, tail split), output type,
+    sign of alpha and beta term.  In round-to-nearest a sum that starts at
+    +0 and cancels is +0 in any order, so the sign is unique; an earlier
+    version of the bit-exact check accepted either sign, which this test
+    would now catch."""
+    g = _gpu()
+    if spec:
+        monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    for out in ("f16", "f32"):
+        A, B, C = _signed_zero_problem(out)
+        At, Bt, Ct = (torch.from_numpy(x).cuda() for x in (A, B, C))
+        for alpha in (1.0, -1.5):
+            for beta in (0.0, 0.5, -1.0):
+                _say(f"[signed zero] {spec or 'planner'} out={out} "
+                     f"alpha={alpha} beta={beta}")
+                D = g.gemm_tn(At, Bt, alpha, beta, Ct if beta else None,
+                              out_dtype=_dt(out))
+                torch.cuda.synchronize()
+                ref = oracle.gemm_tn(A, B, alpha, beta, C if beta else None)
+                zeros = int((ref == 0).sum())
+                assert zeros > 50
+                res = oracle.check_exact(D.cpu().numpy(), ref, out)
+                assert res.ok, f"{spec} {out} a={alpha} b={beta}: {res}"

@@ -35,13 +35,6 @@
 #include <stdlib.h>
 #include <string.h>
 
-/* ORACLE_MUTANT plants a known mistake in a separately built copy (the
- * tests build each one on the CPU and check that the pins reject it).
- * The oracle proper is built with ORACLE_MUTANT == 0. */
-#ifndef ORACLE_MUTANT
-#define ORACLE_MUTANT 0
-#endif
-
 /* ---- IEEE 754 binary16 codec ------------------------------------------ */
 
 /* bits s|e(5)|m(10):  e = 0 -> (-1)^s * m * 2^-24 (zero / subnormal);
@@ -53,7 +46,7 @@ double gemm_oracle_half_to_double(uint16_t h)
     int m = h & 0x3FF;
     double v;
     if (e == 0)
-        v = (ORACLE_MUTANT == 4) ? 0.0 : ldexp((double)m, -24);
+        v = ldexp((double)m, -24);
     else if (e == 31)
         v = (m == 0) ? INFINITY : NAN;
     else
@@ -85,8 +78,7 @@ uint16_t gemm_oracle_double_to_half(double x)
     double fl = floor(t);
     double rem = t - fl;           /* exact */
     double n = fl;
-    if (ORACLE_MUTANT != 5 &&
-        (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0)))
+    if (rem > 0.5 || (rem == 0.5 && fmod(fl, 2.0) != 0.0))
         n = fl + 1.0;
     /* n * q is the rounded magnitude; n may have carried to 2048 */
     double r = n * q;
@@ -144,12 +136,11 @@ static double element(const double *arow, const double *brow, int64_t bstep,
                       int c_dtype, int64_t cidx)
 {
     double s = 0.0;
-    for (int64_t k = 0; k < K - (ORACLE_MUTANT == 1 && K > 0); ++k)
+    for (int64_t k = 0; k < K; ++k)
         s += arow[k] * brow[k * bstep];
     double r = alpha * s;
     if (beta != 0.0)
-        r = (ORACLE_MUTANT == 3) ? r - beta * load_c(C, c_dtype, cidx)
-                                 : r + beta * load_c(C, c_dtype, cidx);
+        r = r + beta * load_c(C, c_dtype, cidx);
     return r;
 }
 
@@ -175,15 +166,11 @@ static void *gemm_worker(void *p)
         r += job->row_begin;
         if (r >= job->row_end)
             break;
-        int64_t bi = (ORACLE_MUTANT == 6) ? 0 : r / job->M;
+        int64_t bi = r / job->M;
         const double *arow = job->a + r * job->K;
         for (int64_t j = 0; j < job->N; ++j) {
             const double *brow = job->b + (bi * job->N + j) * job->K;
             int64_t bstep = 1;
-            if (ORACLE_MUTANT == 2) {          /* B read as K x N */
-                brow = job->b + bi * job->N * job->K + j;
-                bstep = job->N;
-            }
             int64_t cidx = r * job->N + j;
             job->ref[(r - job->row_begin) * job->N + j] =
                 element(arow, brow, bstep, job->K, job->alpha, job->beta,

@@ -38,12 +38,14 @@ CSRC = os.path.join(ROOT, "dense_gemm_fp16_amd", "csrc")
 # device code of the GEMM kernels (host-side planning is not part of it)
 KERNEL_SOURCES = ("gemm_tn_kernels.hpp", "gemm_tn_config.hpp",
                   "gemm_tn_launch.hpp", "gemm_tn_tile256.hip",
-                  "gemm_tn_tile128.hip", "gemm_tn_tile64.hip")
-TRANSPOSE_SOURCES = ("transpose.hip",)
+                  "gemm_tn_tile128.hip", "gemm_tn_tile64.hip",
+                  "lds_layout.hpp")
+TRANSPOSE_SOURCES = ("transpose.hip", "lds_layout.hpp")
 ATTENTION_SOURCES = ("attention_fwd.hip", "gemm_tn_kernels.hpp",
-                     "gemm_tn_config.hpp")
+                     "gemm_tn_config.hpp", "lds_layout.hpp")
 ATTENTIONS = ("attn_64x1024", "attn_small")
-F16ACC_SOURCES = ("gemm_f16acc.hip", "gemm_tn_kernels.hpp", "gemm_tn_config.hpp")
+F16ACC_SOURCES = ("gemm_f16acc.hip", "gemm_tn_kernels.hpp", "gemm_tn_config.hpp",
+                  "lds_layout.hpp")
 # fp16-accumulating GEMMs: name -> (batch, M, N, K)
 F16ACCS = {"f16acc_4096": (1, 4096, 4096, 4096)}
 # fp32 transposes: name -> (batch, M, N)

@@ -70,13 +70,8 @@ struct AttnArgs {
     int q_blocks, batch;
 };
 
-// LDS swizzle of the V tile (64-element = 128-byte rows of keys), for its
-// ds_read_b64_tr_b16 reads: a half wave reads 8 consecutive key rows at one
-// pair of 16-byte chunks (c, c + 1), c even.  Rows of one parity share a
-// 256-byte bank line; XORing the chunk with 2 * ((row / 2) % 4) puts the 4
-// rows of each parity on distinct chunk pairs, so the 32 lanes hit 64
-// distinct banks.
-__device__ inline int v_swizzle(int row) { return 2 * ((row >> 1) & 3); }
+// The V tile's swizzle and read addresses are v_swizzle and
+// v_read_offset (lds_layout.hpp).
 
 __device__ inline f32x4 mfma16(const half8 &a, const half8 &b, const f32x4 &c)
 {
@@ -93,11 +88,11 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     constexpr int KS = kBN / 32;            // key steps of the P V product
     constexpr int TILE = kBN * kD;          // halves per K or V tile
     // After the key loop the same LDS stages each wave's block of O: 32 rows
-    // padded to 144 (fp16) or 272 (fp32) bytes, so that the 16 rows a lane
-    // group writes at one column fall on distinct banks and every row
-    // starts on a 16-byte boundary.
+    // of 128 (fp16) or 256 (fp32) bytes in the GEMM epilogue's layout
+    // (stage_offset), so that the 16 rows a lane group writes at one column,
+    // and the rows a lane group reads back, fall on distinct banks.
     constexpr int ES = OutTraits<OutT>::bytes;
-    constexpr int OROW = kD * ES + 16;                      // bytes per row
+    constexpr int OROW = kD * ES;                           // bytes per row
     constexpr int OWAVE = MI * 16 * OROW;                   // bytes per wave
     constexpr int LDS_HALVES = (4 * TILE > kWaves * OWAVE / 2)
                                    ? 4 * TILE : kWaves * OWAVE / 2;
@@ -191,9 +186,8 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
         for (int s = 0; s < DS; ++s)
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
-                const int row = j * 16 + r16;
                 const half8 kf = *(const half8 *)(
-                    sK + row * kD + swizzle_chunk<kD>(row, 4 * s + g) * 8);
+                    sK + tn_frag_offset<kD, 16>(j * 16, lane, s));
 #pragma unroll
                 for (int i = 0; i < MI; ++i)
                     sacc[i][j] = mfma16(kf, qf[i][s], sacc[i][j]);
@@ -303,13 +297,9 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
     const uint32_t lds_base = (uint32_t)(uintptr_t)(const GTN_LDS void *)lds;
     uint32_t v_addr[DJ];
 #pragma unroll
-    for (int dj = 0; dj < DJ; ++dj) {
-        const int row = 4 * g + (r16 >> 2);
-        const int col = dj * 16 + 4 * (r16 & 3);
-        const int pc = (col >> 3) ^ v_swizzle(row);
-        v_addr[dj] = lds_base +
-                     (uint32_t)((2 * TILE + row * kD + pc * 8 + (col & 7)) * 2);
-    }
+    for (int dj = 0; dj < DJ; ++dj)
+        v_addr[dj] = lds_base + (uint32_t)(2 * TILE * 2) +
+                     v_read_offset<kD>(lane, dj);
     auto read_v = [&](int vs, u32x2 (&vr)[KS * DJ * 2]) {
         const uint32_t so = (uint32_t)(vs * TILE * 2);
 #pragma unroll
@@ -467,7 +457,8 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
 #pragma unroll
         for (int dj = 0; dj < DJ; ++dj) {
             const f32x4 o = oacc[i][dj] * inv;
-            char *dst = ob + (i * 16 + r16) * OROW + (dj * 16 + 4 * g) * ES;
+            char *dst = ob + stage_offset<OROW>(i * 16 + r16,
+                                                (dj * 16 + 4 * g) * ES);
             if constexpr (ES == 2) {
                 const half4 h = {(_Float16)o[0], (_Float16)o[1],
                                  (_Float16)o[2], (_Float16)o[3]};
@@ -489,7 +480,7 @@ __global__ void __launch_bounds__(kWaves * 64) attn_fwd_kernel(AttnArgs p)
 #pragma unroll
     for (int it = 0; it < MI * 16 / RPI; ++it) {
         const int row = it * RPI + lane / LPR, ch = lane % LPR;
-        const u32x4 v = *(const u32x4 *)(ob + row * OROW + ch * 16);
+        const u32x4 v = *(const u32x4 *)(ob + stage_offset<OROW>(row, ch * 16));
         __builtin_amdgcn_raw_buffer_store_b128(
             v, rO, (uint32_t)(row * kD * ES + ch * 16), 0, GTN_STORE_CPOL);
     }

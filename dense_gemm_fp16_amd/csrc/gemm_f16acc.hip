@@ -148,22 +148,15 @@ __global__ void __launch_bounds__(kThr) gemm_f16acc_kernel(AccArgs p)
     auto step = [&](int stage, int s) {
         const _Float16 *sA = lds + stage * 2 * TILE;
         const _Float16 *sB = sA + TILE;
-        const int k = 16 * s + 4 * fg;              // this lane's 4 k
-        half4v af[4], bf[4];
+        half4v af[4], bf[4];                        // 4 k per lane
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = wm * 64 + i * 16 + fr;
-            af[i] = *(const half4v *)(sA + row * kBKa +
-                                      swizzle_chunk<kBKa>(row, k >> 3) * 8 +
-                                      (k & 7));
-        }
+        for (int i = 0; i < 4; ++i)
+            af[i] = *(const half4v *)(sA + tn_frag4_offset<kBKa>(
+                                               wm * 64 + i * 16, lane, s));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int row = wn * 64 + j * 16 + fr;
-            bf[j] = *(const half4v *)(sB + row * kBKa +
-                                      swizzle_chunk<kBKa>(row, k >> 3) * 8 +
-                                      (k & 7));
-        }
+        for (int j = 0; j < 4; ++j)
+            bf[j] = *(const half4v *)(sB + tn_frag4_offset<kBKa>(
+                                               wn * 64 + j * 16, lane, s));
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll

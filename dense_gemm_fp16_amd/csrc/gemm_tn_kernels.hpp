@@ -49,6 +49,7 @@
 #include <stdint.h>
 
 #include "gemm_tn_config.hpp"
+#include "lds_layout.hpp"
 
 namespace gtn {
 
@@ -127,39 +128,6 @@ __device__ inline TileCoord map_tile(const GemmArgs &p)
     tc.tm = first_m + in_g % rows_in_group;
     tc.tn = in_g / rows_in_group;
     return tc;
-}
-
-// LDS swizzle of a tile with BK-element (2*BK-byte) rows.  gfx950's LDS has
-// 64 banks of 4 bytes and serves a ds_read_b128 16 lanes (256 bytes) at a
-// time, so the 16 rows read together by one lane group must fill the 16
-// distinct 16-byte bank slots of a 256-byte line.  A 256-byte line holds
-// R = 128 / BK rows; XORing the chunk index with (row / R) mod CHUNKS makes
-// the R rows of a line and the CHUNKS lines of a 16-row group land in
-// distinct slots for every logical chunk.  (Measured on MI355X: zero
-// SQ_LDS_BANK_CONFLICT with this map, half of all LDS cycles in conflict
-// with row mod 8, the map a 32-bank LDS would want.)
-template <int BK>
-__device__ __host__ constexpr int swizzle_chunk(int row, int chunk)
-{
-    return chunk ^ ((row / (128 / BK)) % (BK / 8));
-}
-
-// LDS swizzle of an operand tile stored along M (N): BK rows of k, each
-// CR = BM / 8 chunks of 16 bytes (8 consecutive m).  Its fragments are read
-// with ds_read_b64_tr_b16, where lane group g of a wave reads rows
-// 8g + 4r + (0..3) of a k-step, 32 bytes each; a half wave thus touches 8
-// rows {0..3, 8..11} (+4, +16, +32 ...) at one pair of chunks (c, c+1),
-// and XORing the chunk with 2*h(row) (h distinct over those 8 rows, and
-// kept below CR so the pair stays adjacent and in its 256-byte line) puts
-// them in distinct bank slots.  With 128-byte rows two rows share a
-// 256-byte line by parity, so h only has to separate rows of one parity.
-template <int CR>
-__device__ __host__ constexpr int swizzle_mn(int row, int chunk)
-{
-    static_assert(CR == 8 || CR % 16 == 0, "rows of 128 bytes or 256n");
-    return CR >= 16
-               ? chunk ^ (2 * ((row & 3) | (((row >> 3) & 1) << 2)))
-               : chunk ^ (2 * (((row >> 1) & 1) | (((row >> 3) & 1) << 1)));
 }
 
 template <bool V>
@@ -625,8 +593,6 @@ gemm_tn_kernel(GemmArgs p)
     };
 
     // ---- LDS -> registers, and the MFMAs of one KM-wide k-step ---------
-    const int frow = lane % MB;
-    const int fq = lane / MB;
     // Fragment of an operand tile stored along M (N) (BK rows of W
     // elements): rows c0 .. c0 + 15, the 32 k of k-step ks.  Each
     // ds_read_b64_tr_b16 gives lane i of every 16-lane group the 4 values
@@ -646,16 +612,10 @@ gemm_tn_kernel(GemmArgs p)
     const uint32_t lds_addr = (uint32_t)(uintptr_t)(const GTN_LDS void *)lds;
     auto read_tr = [&](auto w_tag, int tile, int cbase, int f, auto ks_tag) {
         constexpr int W = decltype(w_tag)::value;
-        constexpr int CR = W / 8;
         constexpr int KS = decltype(ks_tag)::value;
         static_assert(KM == 32 && MB == 16, "k-steps of 32, 16-wide blocks");
-        const int i = lane & 15, g = lane >> 4;
-        const int row = 8 * g + (i >> 2);
-        const uint32_t q0 =
-            (uint32_t)((2 * cbase) ^ (swizzle_mn<CR>(row, 0) * 16));
-        const uint32_t base =
-            lds_addr + (uint32_t)((tile + row * W) * 2) +
-            (uint32_t)(16 * ((i & 3) >> 1) + 8 * (i & 1)) + q0;
+        const uint32_t base = lds_addr + (uint32_t)(tile * 2) +
+                              tr_read_offset<W>(lane, cbase);
         const uint32_t addr = base ^ (uint32_t)(32 * f);
         const u32x2 lo = ds_read_tr_asm<KS * 32 * W * 2>(addr);
         const u32x2 hi = ds_read_tr_asm<(KS * 32 + 4) * W * 2>(addr);
@@ -686,23 +646,20 @@ gemm_tn_kernel(GemmArgs p)
                            half8 (&bf)[NI]) {
         const _Float16 *sA = lds + a_base(sta);
         const _Float16 *sB = lds + b_base(stb);
-        const int ch = ks * QN + fq;
         auto rd_a = [&](int i) {
             if constexpr (A_TR) {
                 af[i] = read_tr(Int<BM>{}, a_base(sta), wm * WTM, i, ks);
             } else {
-                const int row = wm * WTM + i * MB + frow;
-                af[i] = *(const half8 *)(sA + row * BK +
-                                         swizzle_chunk<BK>(row, ch) * 8);
+                af[i] = *(const half8 *)(sA + tn_frag_offset<BK, MB>(
+                                                  wm * WTM + i * MB, lane, ks));
             }
         };
         auto rd_b = [&](int j) {
             if constexpr (B_TR) {
                 bf[j] = read_tr(Int<BN>{}, b_base(stb), wn * WTN, j, ks);
             } else {
-                const int row = wn * WTN + j * MB + frow;
-                bf[j] = *(const half8 *)(sB + row * BK +
-                                         swizzle_chunk<BK>(row, ch) * 8);
+                bf[j] = *(const half8 *)(sB + tn_frag_offset<BK, MB>(
+                                                  wn * WTN + j * MB, lane, ks));
             }
         };
         rd_b(0);
@@ -974,15 +931,10 @@ gemm_tn_kernel(GemmArgs p)
     constexpr int FIT = REGION / ROW_BYTES / 32 * 32;
     constexpr int RPP = FIT < WTM ? FIT : WTM;        // rows per pass
     constexpr int PASSES = WTM / RPP;
-    constexpr int LINE_ROWS = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
     static_assert(RPP >= 32 && WTM % RPP == 0, "LDS slice holds 32-row bands");
     static_assert(RPP * CPR % 64 == 0, "whole waves of 16-byte chunks");
-    // Chunk c of staged row r sits at chunk c ^ ((r / LINE_ROWS) % CPR'):
-    // the rows a store instruction writes spread over distinct banks.
-    auto stage_chunk = [](int r, int c) {
-        constexpr int X = CPR < 16 ? CPR : 16;
-        return c ^ ((r / LINE_ROWS) % X);
-    };
+    // Staged rows are laid out by stage_offset (lds_layout.hpp): the rows
+    // a store instruction writes spread over distinct banks.
     char *region = (char *)lds + wave * REGION;
 
     // Fp32 results of the block in output precision, then into the slice.
@@ -1000,8 +952,7 @@ gemm_tn_kernel(GemmArgs p)
                     const int r = ii * MB + em;
                     const int col = j * MB + 4 * QN * g + en;  // element column
                     const int cb = col * ES;                  // byte column
-                    char *dst = region + r * ROW_BYTES +
-                                stage_chunk(r, cb / 16) * 16 + cb % 16;
+                    char *dst = region + stage_offset<ROW_BYTES>(r, cb);
                     if (ES == 4) {
                         *(f32x4 *)dst = v;
                     } else {
@@ -1019,8 +970,8 @@ gemm_tn_kernel(GemmArgs p)
         for (int it = 0; it < RPP * CPR / 64; ++it) {
             const int idx = it * 64 + lane;
             const int r = idx / CPR, c = idx % CPR;
-            const u32x4 v = *(const u32x4 *)(region + r * ROW_BYTES +
-                                             stage_chunk(r, c) * 16);
+            const u32x4 v =
+                *(const u32x4 *)(region + stage_offset<ROW_BYTES>(r, c * 16));
             const int lm = wm * WTM + pass * RPP + r;
             const int64_t n = n0 + wn * WTN + c * (16 / ES);
             const uint32_t off =
@@ -1104,8 +1055,7 @@ gemm_tn_kernel(GemmArgs p)
                 const int idx = it * 64 + lane;
                 const int r = idx / EPR, ce = idx % EPR;
                 const int cb = ce * ES;               // byte column
-                const char *src = region + r * ROW_BYTES +
-                                  stage_chunk(r, cb / 16) * 16 + cb % 16;
+                const char *src = region + stage_offset<ROW_BYTES>(r, cb);
                 const int lm = wm * WTM + pass * RPP + r;
                 const int64_t n = n0 + wn * WTN + ce;
                 const uint32_t off =

@@ -19,9 +19,12 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "lds_layout.hpp"
 #include "transpose_f32.h"
 
 namespace {
+
+using gtn::transpose_word;
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -80,14 +83,14 @@ transpose_f32_kernel(const float *x, float *y, int64_t M, int64_t N,
                 f32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                tile[r * kT + ((4 * c + e) ^ r)] = v[e];
+                tile[transpose_word<kT>(r, 4 * c + e)] = v[e];
         } else {
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t off = 4 * c + e < cols_left
                                          ? (uint32_t)((r * N + 4 * c + e) * 4)
                                          : kOob;
-                tile[r * kT + ((4 * c + e) ^ r)] = __builtin_bit_cast(
+                tile[transpose_word<kT>(r, 4 * c + e)] = __builtin_bit_cast(
                     float, __builtin_amdgcn_raw_buffer_load_b32(rx, off, 0, 0));
             }
         }
@@ -108,7 +111,7 @@ transpose_f32_kernel(const float *x, float *y, int64_t M, int64_t N,
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int ii = 4 * q + e;
-            v[e] = tile[ii * kT + (jj ^ ii)];
+            v[e] = tile[transpose_word<kT>(ii, jj)];
         }
         if (VEC) {
             const uint32_t off = 4 * q < rows_left

@@ -25,7 +25,11 @@ LIB_PATH = os.path.join(_HERE, "libgemm_tn.so")
 
 GEMM_TN_F16, GEMM_TN_F32 = 0, 1
 GEMM_TN_ROW_K, GEMM_TN_ROW_MN = 0, 1
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(5)
+(OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE,
+ ERR_SCRATCH) = range(6)
+# fixed per-GPU split-K scratch of gemm_tn_ex_noalloc (GEMM_TN_NOALLOC_
+# SCRATCH_BYTES in include/gemm_tn.h)
+NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
 
 # torch bundles its own HIP runtime under the same soname as the system one
 # (libamdhip64.so.7).  Whichever is loaded first serves the whole process, so
@@ -34,7 +38,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_LAUNCH, ERR_WORKSPACE = range(5)
 import torch  # noqa: E402,F401
 
 EXPORTS = ("gemm_tn", "gemm_tn_strided_batched", "gemm_tn_ex",
-           "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version",
+           "gemm_tn_ex_noalloc", "gemm_tn_describe", "gemm_tn_status_string", "gemm_tn_version",
            "transpose_f32", "attention_fwd", "gemm_tn_f16acc")
 
 _REBUILD = ("run `python dense_gemm_fp16_amd/build.py` "
@@ -60,6 +64,8 @@ _lib.gemm_tn_ex.restype = _int
 _lib.gemm_tn_ex.argtypes = [_i64, _i64, _i64, _i64, _f32, _vp, _int, _i64,
                             _i64, _vp, _int, _i64, _i64, _f32, _vp, _i64, _i64,
                             _vp, _i64, _i64, _int, _vp]
+_lib.gemm_tn_ex_noalloc.restype = _int
+_lib.gemm_tn_ex_noalloc.argtypes = _lib.gemm_tn_ex.argtypes
 _lib.gemm_tn_describe.restype = _int
 _lib.gemm_tn_describe.argtypes = [_i64, _i64, _i64, _i64, _int, _i64, _int,
                                   _i64, _i64, _i64, _i64, _i64, _i64, _i64,
@@ -249,6 +255,20 @@ def gemm_tn_ex(batch, M, N, K, alpha, A_ptr, lda, strideA, B_ptr, ldb,
                            strideA, B_ptr, layout_b, ldb, strideB,
                            float(beta), C_ptr, ldc, strideC, D_ptr, ldd,
                            strideD, d_dtype, stream_handle)
+
+
+def gemm_tn_ex_noalloc(batch, M, N, K, alpha, A_ptr, lda, strideA, B_ptr, ldb,
+                       strideB, beta, C_ptr, ldc, strideC, D_ptr, ldd,
+                       strideD, d_dtype, stream_handle, layout_a=GEMM_TN_ROW_K,
+                       layout_b=GEMM_TN_ROW_K) -> int:
+    """Raw-pointer call of gemm_tn_ex_noalloc() (split-K partials in the
+    library's fixed per-GPU scratch, no allocation); returns the status
+    code."""
+    return _lib.gemm_tn_ex_noalloc(batch, M, N, K, float(alpha), A_ptr,
+                                   layout_a, lda, strideA, B_ptr, layout_b,
+                                   ldb, strideB, float(beta), C_ptr, ldc,
+                                   strideC, D_ptr, ldd, strideD, d_dtype,
+                                   stream_handle)
 
 
 def transpose_f32(x, out=None, stream=None):

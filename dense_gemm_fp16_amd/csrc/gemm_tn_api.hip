@@ -73,6 +73,42 @@ int get_workspace(hipStream_t s, int64_t bytes, float **out,
     return GEMM_TN_OK;
 }
 
+// Scratch of gemm_tn_ex_noalloc: the split-K partials of callers that
+// cannot allocate live in this fixed array instead of the per-stream
+// workspace.  Each GPU the library runs on holds its own copy for the life
+// of the process.  In host code `scratch` names a host-side stand-in, not
+// device memory: its device address on the current GPU comes from
+// hipGetSymbolAddress, taken once per device and kept in g_scratch_dev.
+static __device__ __align__(256) char scratch[GEMM_TN_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_lock;
+void *g_scratch_dev[kMaxDevices];
+
+// The current device's address of `scratch`, for a problem needing `bytes`
+// of it.  No allocation: the array exists once the library's code object
+// is loaded on the device.
+int get_static_scratch(int64_t bytes, float **out)
+{
+    if (bytes > GEMM_TN_NOALLOC_SCRATCH_BYTES)
+        return GEMM_TN_ERR_SCRATCH;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return GEMM_TN_ERR_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_scratch_lock);
+    if (g_scratch_dev[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess ||
+            ptr == nullptr) {
+            (void)hipGetLastError();
+            return GEMM_TN_ERR_LAUNCH;
+        }
+        g_scratch_dev[dev] = ptr;
+    }
+    *out = (float *)g_scratch_dev[dev];
+    return GEMM_TN_OK;
+}
+
 bool aligned(const void *p, uintptr_t a)
 {
     return ((uintptr_t)p % a) == 0;
@@ -132,7 +168,7 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
         const void *A, int layout_a, int64_t lda, int64_t sA, const void *B,
         int layout_b, int64_t ldb, int64_t sB, float beta, const void *C,
         int64_t ldc, int64_t sC, void *D, int64_t ldd, int64_t sD,
-        int d_dtype, void *stream)
+        int d_dtype, void *stream, bool noalloc)
 {
     if (!layout_ok(layout_a) || !layout_ok(layout_b))
         return GEMM_TN_ERR_INVALID_ARG;
@@ -187,7 +223,8 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.group_m = p.group_m;
     std::unique_lock<std::mutex> ws_lock;   // held until the launches
     if (p.splits > 1 || p.tail_rows > 0) {
-        st = get_workspace(s, p.ws_bytes, &a.ws, ws_lock);
+        st = noalloc ? get_static_scratch(p.ws_bytes, &a.ws)
+                     : get_workspace(s, p.ws_bytes, &a.ws, ws_lock);
         if (st != GEMM_TN_OK)
             return st;
     }
@@ -229,7 +266,7 @@ int gemm_tn(int64_t M, int64_t N, int64_t K, float alpha, const void *A,
 {
     return gtn::run(1, M, N, K, alpha, A, GEMM_TN_ROW_K, K, 0, B,
                     GEMM_TN_ROW_K, K, 0, beta, C, N, 0, D, N, 0, d_dtype,
-                    stream);
+                    stream, false);
 }
 
 int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -240,7 +277,7 @@ int gemm_tn_strided_batched(int64_t batch, int64_t M, int64_t N, int64_t K,
 {
     return gtn::run(batch, M, N, K, alpha, A, GEMM_TN_ROW_K, K, strideA, B,
                     GEMM_TN_ROW_K, K, strideB, beta, C, N, strideC, D, N,
-                    strideD, d_dtype, stream);
+                    strideD, d_dtype, stream, false);
 }
 
 int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
@@ -252,7 +289,20 @@ int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
 {
     return gtn::run(batch, M, N, K, alpha, A, layout_a, lda, strideA, B,
                     layout_b, ldb, strideB, beta, C, ldc, strideC, D, ldd,
-                    strideD, d_dtype, stream);
+                    strideD, d_dtype, stream, false);
+}
+
+int gemm_tn_ex_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void *A, int layout_a, int64_t lda,
+                       int64_t strideA, const void *B, int layout_b,
+                       int64_t ldb, int64_t strideB, float beta,
+                       const void *C, int64_t ldc, int64_t strideC, void *D,
+                       int64_t ldd, int64_t strideD, int d_dtype,
+                       void *stream)
+{
+    return gtn::run(batch, M, N, K, alpha, A, layout_a, lda, strideA, B,
+                    layout_b, ldb, strideB, beta, C, ldc, strideC, D, ldd,
+                    strideD, d_dtype, stream, true);
 }
 
 int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
@@ -293,11 +343,14 @@ const char *gemm_tn_status_string(int status)
         return "kernel launch failed";
     case GEMM_TN_ERR_WORKSPACE:
         return "split-K workspace allocation failed";
+    case GEMM_TN_ERR_SCRATCH:
+        return "problem needs more split-K scratch than "
+               "gemm_tn_ex_noalloc's static maximum";
     default:
         return "unknown status";
     }
 }
 
-int gemm_tn_version(void) { return (1 << 16) | 1; }
+int gemm_tn_version(void) { return (1 << 16) | 2; }
 
 }  // extern "C"

@@ -87,9 +87,15 @@ typedef enum gemm_tn_status {
                                     along M / N), N or a C/D row stride >
                                     2^20, or M > 2^31 - 1 */
     GEMM_TN_ERR_LAUNCH = 3,      /* the HIP runtime rejected a launch */
-    GEMM_TN_ERR_WORKSPACE = 4    /* the split-K workspace could not be
+    GEMM_TN_ERR_WORKSPACE = 4,   /* the split-K workspace could not be
                                     allocated */
+    GEMM_TN_ERR_SCRATCH = 5      /* gemm_tn_ex_noalloc: the problem's
+                                    split-K plan needs more than
+                                    GEMM_TN_NOALLOC_SCRATCH_BYTES */
 } gemm_tn_status;
+
+/* Size of the fixed per-GPU scratch of gemm_tn_ex_noalloc (16 MiB). */
+#define GEMM_TN_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
 
 /*
  * One GEMM.  M, N, K >= 0.
@@ -152,6 +158,33 @@ int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
                void *stream);
 
 /*
+ * gemm_tn_ex for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, kernels and results (bit for bit) as
+ * gemm_tn_ex.  Where gemm_tn_ex would allocate or grow its per-stream
+ * split-K workspace (skinny problems split along K, and the tail split of
+ * a grid ending in a mostly idle wave), this entry point uses a fixed
+ * device array of GEMM_TN_NOALLOC_SCRATCH_BYTES instead, one per GPU,
+ * held until the process ends; it calls no hipMalloc or hipFree.
+ *   - A problem whose plan needs more partials than that (splits x batch x
+ *     M x round_up(N, 4) x 4 bytes, or the tail rows' share) returns
+ *     GEMM_TN_ERR_SCRATCH and launches nothing.
+ *   - Every call on one GPU shares that GPU's array: calls that overlap on
+ *     one GPU (several streams or host threads at once) race on it, and
+ *     the caller must order them.  Nothing in it has to start at zero: each
+ *     call writes every partial it reads.
+ *   - The array's device address is looked up once per device, on the
+ *     first call with that device current.
+ */
+int gemm_tn_ex_noalloc(int64_t batch, int64_t M, int64_t N, int64_t K,
+                       float alpha, const void *A, int layout_a, int64_t lda,
+                       int64_t strideA, const void *B, int layout_b,
+                       int64_t ldb, int64_t strideB, float beta,
+                       const void *C, int64_t ldc, int64_t strideC, void *D,
+                       int64_t ldd, int64_t strideD, int d_dtype,
+                       void *stream);
+
+/*
  * Name of the kernel configuration gemm_tn_ex would launch for this
  * problem (tile shape, loader, split-K factor, and the tail split: the
  * number of bottom tile rows split along K and into how many slices),
@@ -169,7 +202,7 @@ int gemm_tn_describe(int64_t batch, int64_t M, int64_t N, int64_t K,
 /* Human-readable text of a status code (static storage). */
 const char *gemm_tn_status_string(int status);
 
-/* Library ABI version: (major << 16) | minor (currently 1.1). */
+/* Library ABI version: (major << 16) | minor (currently 1.2). */
 int gemm_tn_version(void);
 
 #ifdef __cplusplus

@@ -40,7 +40,7 @@ def test_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert g.version() == (1, 1)
+    assert g.version() == (1, 2)
     assert g.status_string(OK) == "ok"
     assert g.status_string(INVALID) == "invalid argument"
     assert g.status_string(99) == "unknown status"
@@ -342,3 +342,18 @@ def test_f16acc_broadcast_strides_are_accepted_by_the_checks():
     # so use the overlap check to see that a 0 stride is not rejected)
     assert _acc(sA=0, d=0x100000 + 64) == INVALID     # still overlaps A
     assert _acc(batch=0, sA=0, sB=0) == OK
+
+
+def test_noalloc_rejects_plans_beyond_its_scratch():
+    """gemm_tn_ex_noalloc refuses, before any launch, a problem whose
+    split-K partials exceed its fixed scratch: the tail split of 4352^2 x
+    4096 needs 4 slices x 512 rows x 4352 x 4 bytes = 35.7 MB > 16 MiB."""
+    M = N = 4352
+    K = 4096
+    st = g.gemm_tn_ex_noalloc(1, M, N, K, 1.0, P, K, M * K, P, K, N * K, 0.0,
+                              NULL, N, M * N, P, N, M * N, F32, S)
+    assert st == g.ERR_SCRATCH
+    assert "static maximum" in g.status_string(st)
+    # argument errors are still reported first
+    assert g.gemm_tn_ex_noalloc(1, -1, N, K, 1.0, P, K, 0, P, K, 0, 0.0, NULL,
+                                N, 0, P, N, 0, F32, S) == INVALID

@@ -8,7 +8,14 @@ synthetic inputs, already resident in HBM.  The default workload is the
 compute-bound 4096 x 4096 x 4096 product with fp16 D.  The timed region is
 K back-to-back calls on one stream, bracketed by device synchronisations,
 and timed with HIP events recorded on that same stream.  One JSON line goes
-to stdout; `--all` adds a table of every workload on stderr.
+to stdout.  `--all` first prints one JSON record per configuration of the
+study (256^3, 1024^3 with C, 4096^3, 1000x1030x1000, 128x4096x8192, the
+64-batch score product), each with TFLOP/s, GB/s, both roofline fractions,
+and the CPU oracle run over every output on the host's cores (its time is
+the record's CPU baseline; its results check the GPU output, and the
+integer variant's bit for bit); `--extras` adds a stderr table of the other
+workloads.  Under `rocprofv3 --kernel-trace`, `--summarize-trace-all`
+turns the trace of such a run into per-configuration kernel times.
 
 The fp32 transpose of the pages is measured the same way with
 `--workload transpose_1024` (their 1024 x 1024 case) or `transpose_8192`
@@ -164,7 +171,18 @@ def _args():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="c3_4096")
     ap.add_argument("--all", action="store_true",
-                    help="also time every workload (stderr table)")
+                    help="first print one JSON record per configuration of "
+                         "the study (c1 ... c5), each with its full-output "
+                         "oracle run as CPU baseline and parity check")
+    ap.add_argument("--extras", action="store_true",
+                    help="also time the workloads beyond the study's "
+                         "configurations (stderr table)")
+    ap.add_argument("--summarize-trace-all", nargs="+",
+                    metavar=("KERNEL_TRACE_CSV", "BENCH_JSONL"),
+                    help="per-configuration kernel times from a rocprofv3 "
+                         "kernel_trace.csv of a --all run (markdown table; "
+                         "with the run's stdout, its HIP-event times and "
+                         "oracle times beside them)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
@@ -199,8 +217,9 @@ def _device_inputs(w, torch):
     return A, B, C, D
 
 
-def time_workload(w, steps, warmup):
-    """Average time of one call (seconds), HIP events on the launch stream."""
+def time_workload(w, steps, warmup, return_output=False):
+    """Average time of one call (seconds), HIP events on the launch stream
+    (and the output of the last call, on the host, with return_output)."""
     import torch
     import dense_gemm_fp16_amd as g
     A, B, C, D = _device_inputs(w, torch)
@@ -213,6 +232,39 @@ def time_workload(w, steps, warmup):
     start.record(stream)
     for _ in range(steps):
         g.gemm_tn(A, B, w.alpha, w.beta, C, out=D, stream=stream)
+    stop.record(stream)
+    torch.cuda.synchronize()
+    sec = start.elapsed_time(stop) / 1e3 / steps
+    if return_output:
+        return sec, D.cpu().numpy()
+    return sec
+
+
+def time_workload_graph(w, steps, warmup):
+    """Average time of one call (seconds) when `steps` back-to-back calls
+    are captured into one HIP graph and the graph is replayed: the GPU-side
+    time per call without the host's per-call cost (argument checks,
+    planning, the launch through the binding), which bounds small
+    problems when they are called one by one."""
+    import torch
+    import dense_gemm_fp16_amd as g
+    A, B, C, D = _device_inputs(w, torch)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for _ in range(max(warmup, 1)):   # plans and workspaces made here
+            g.gemm_tn(A, B, w.alpha, w.beta, C, out=D)
+    stream.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph, stream=stream):
+        for _ in range(steps):
+            g.gemm_tn(A, B, w.alpha, w.beta, C, out=D)
+    graph.replay()                        # first replay uploads the graph
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    with torch.cuda.stream(stream):
+        graph.replay()
     stop.record(stream)
     torch.cuda.synchronize()
     return start.elapsed_time(stop) / 1e3 / steps
@@ -270,6 +322,84 @@ def summarize_trace(csv_path, workload):
             "min_ns": ns[0] if ns else None, "max_ns": ns[-1] if ns else None}
 
 
+def trace_signatures(w):
+    """(kernel name part, Grid_Size_X, Workgroup_Size_X) of every kernel one
+    call of workload w launches, from the plan describe() reports: the tile
+    kernel (512 threads on the 256 tile, 256 on the others), the split-K
+    reduction, and for a tail split the tail rows' kernel and reduction."""
+    kv = dict(x.split("=", 1) for x in describe(w).split())
+    bm = int(kv["tile"].split("x")[0])
+    wg = 512 if bm == 256 else 256
+
+    def reduce_sig(rows):
+        work = w.batch * rows * ((w.N + 3) // 4)
+        return ("splitk_reduce", (work + 255) // 256 * 256, 256)
+
+    sigs = [("gemm_tn_kernel", int(kv["grid"]) * wg, wg)]
+    if int(kv["split"]) > 1:
+        sigs.append(reduce_sig(w.M))
+    tail_rows = int(kv["tail_rows"])
+    if tail_rows > 0:
+        sigs.append(("gemm_tn_kernel", int(kv["tail_grid"]) * wg, wg))
+        sigs.append(reduce_sig(w.M - (-(-w.M // bm) - tail_rows) * bm))
+    return sigs
+
+
+def summarize_trace_all(csv_path, bench_jsonl=None):
+    """Markdown table of the kernel times of every configuration in one
+    rocprofv3 kernel trace (a --all run): each kernel of a call is found by
+    its signature (trace_signatures), and a call's time is the sum of its
+    kernels' medians.  With the run's stdout, the HIP-event time per call
+    and the oracle's time are set beside them."""
+    import csv
+    import statistics
+    import seeded_inputs as si
+    rows = list(csv.DictReader(open(csv_path)))
+    recs = {}
+    if bench_jsonl:
+        for line in open(bench_jsonl):
+            line = line.strip()
+            if line.startswith("{"):
+                r = json.loads(line)
+                if r.get("record") == "config":
+                    recs[r["workload"]] = r
+    out = ["| config | kernels (grid threads) | launches | kernel median "
+           "us | min us | TFLOP/s | % MFMA peak | GB/s | % HBM | HIP events "
+           "us per call | oracle s (threads) | parity float / int |",
+           "|---|---|---|---|---|---|---|---|---|---|---|---|"]
+    for name in CONFIGS:
+        w = si.workload_shape(name)
+        med = mins = 0.0
+        launches = []
+        for part, grid, wg in trace_signatures(w):
+            d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+                 for r in rows
+                 if part in r["Kernel_Name"]
+                 and int(r["Grid_Size_X"]) == grid
+                 and int(r["Workgroup_Size_X"]) == wg]
+            if not d:
+                raise SystemExit(f"{name}: no {part} dispatch of grid {grid}")
+            med += statistics.median(d)
+            mins += min(d)
+            launches.append(f"{part} ({grid})")
+            n = len(d)
+        us = med / 1e3
+        rec = recs.get(name, {})
+        cb = rec.get("cpu_baseline", {})
+        par = rec.get("parity", {})
+        out.append(
+            f"| {name} | {', '.join(launches)} | {n} | {us:.2f} | "
+            f"{mins / 1e3:.2f} | {w.flops / us / 1e6:.1f} | "
+            f"{100 * w.flops / us / 1e6 / PEAK_F16_MFMA_TFLOPS:.2f} | "
+            f"{w.algorithmic_bytes / us / 1e3:.0f} | "
+            f"{100 * w.algorithmic_bytes / us / 1e3 / PEAK_HBM_GBS:.1f} | "
+            f"{rec.get('us_per_call', '-')} | "
+            f"{cb.get('seconds', '-')} ({cb.get('cores', '-')}) | "
+            f"{par.get('float_within_tolerance', '-')} / "
+            f"{par.get('integer_bit_exact', '-')} |")
+    return "\n".join(out)
+
+
 def _cpu_model() -> str:
     """The host CPU's model name (/proc/cpuinfo), else the architecture."""
     try:
@@ -280,6 +410,119 @@ def _cpu_model() -> str:
     except OSError:
         pass
     return platform.processor() or platform.machine()
+
+
+def _host_cpus():
+    """(threads the oracle uses, CPUs this process may run on, CPUs the
+    host has).  The oracle's threads are capped at 16, the CPU share the
+    measurement host grants one GPU."""
+    import oracle
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+    return oracle.default_threads(), affinity, os.cpu_count() or 1
+
+
+def oracle_full_check(w, d, exact):
+    """The oracle over every output of w, in blocks of 1024 flattened rows,
+    checked against the GPU result d (tolerance, or bit for bit with
+    exact).  Returns (seconds spent in the oracle, threads, passed, the
+    worst block's result text)."""
+    import oracle
+    threads = oracle.default_threads()
+    flat = np.asarray(d).reshape(w.batch * w.M, w.N)
+    spent, ok, worst = 0.0, True, ""
+    for r0 in range(0, w.batch * w.M, 1024):
+        r1 = min(r0 + 1024, w.batch * w.M)
+        t = time.perf_counter()
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C, rows=(r0, r1),
+                             threads=threads)
+        spent += time.perf_counter() - t
+        res = (oracle.check_exact(flat[r0:r1], ref, w.out_dtype) if exact
+               else oracle.check(flat[r0:r1], ref, w.K, w.out_dtype))
+        if not res.ok or not worst:
+            worst = str(res)
+        ok = ok and res.ok
+    return spent, threads, ok, worst
+
+
+def roofline_of(w, sec, traffic=None):
+    """The workload's bound by arithmetic intensity, and both fractions."""
+    tflops = w.flops / sec / 1e12
+    gbs = w.algorithmic_bytes / sec / 1e9
+    compute_bound = w.flops / w.algorithmic_bytes > (
+        PEAK_F16_MFMA_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
+    if compute_bound:
+        roof = {"bound": "mfma", "achieved": round(tflops, 2),
+                "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4)}
+    else:
+        roof = {"bound": "hbm", "achieved": round(gbs, 1),
+                "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(gbs / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = round(traffic["bytes_per_launch"]) if traffic else None
+    return tflops, gbs, roof
+
+
+# The configurations of the study, in the order of the survey's table.
+CONFIGS = ("c1_256", "c2_1024", "c3_4096", "c4a_ragged", "c4b_skinny",
+           "c5_qk")
+
+
+def config_record(name, steps, warmup, cpu=True):
+    """One JSON record for one configuration: GPU time per call (HIP events
+    over `steps` back-to-back calls), TFLOP/s and GB/s with both roofline
+    fractions, and, with cpu, the oracle over every output on the host's
+    cores (its time is the CPU baseline; its results check the GPU's, in
+    float within tolerance and, for the integer variant, bit for bit)."""
+    import dense_gemm_fp16_amd as g
+    import seeded_inputs as si
+    w = si.workload(name)
+    sec, d = time_workload(w, steps, warmup, return_output=True)
+    gsec = time_workload_graph(w, steps, warmup)
+    tflops, gbs, roof = roofline_of(w, sec, load_traffic(name))
+    rec = {"record": "config", "workload": name,
+           "shape": {"batch": w.batch, "M": w.M, "N": w.N, "K": w.K,
+                     "alpha": w.alpha, "beta": w.beta, "out": w.out_dtype},
+           "kernel": describe(w), "steps": steps, "warmup": warmup,
+           "us_per_call": round(sec * 1e6, 3),
+           "us_per_call_graph": round(gsec * 1e6, 3),
+           "tflops_graph": round(w.flops / gsec / 1e12, 2),
+           "gbs_graph": round(w.algorithmic_bytes / gsec / 1e9, 1),
+           "tflops": round(tflops, 2),
+           "pct_mfma_peak": round(100 * tflops / PEAK_F16_MFMA_TFLOPS, 2),
+           "gbs": round(gbs, 1),
+           "pct_hbm_peak": round(100 * gbs / PEAK_HBM_GBS, 2),
+           "roofline": roof}
+    if cpu:
+        spent, threads, ok, worst = oracle_full_check(w, d, exact=False)
+        wi = si.workload(name, int_values=True)
+        di = run_once(wi)
+        _, _, ok_i, worst_i = oracle_full_check(wi, di, exact=True)
+        used, affinity, host = _host_cpus()
+        rec["parity"] = {"float_within_tolerance": ok, "float": worst,
+                         "integer_bit_exact": ok_i, "integer": worst_i,
+                         "elements": w.batch * w.M * w.N}
+        rec["cpu_baseline"] = {
+            "value": w.flops / spent / 1e12, "unit": "TFLOP/s",
+            "cores": threads, "affinity_cpus": affinity, "host_cpus": host,
+            "kind": "oracle", "seconds": round(spent, 3),
+            "sample": f"every output ({w.batch}x{w.M}x{w.N}x{w.K}, fp64 "
+                      f"sequential k-sum) on {threads} threads of "
+                      f"{_cpu_model()}; {w.flops / spent / 1e9:.1f} GFLOP/s",
+            "gpu_speedup": round(spent / sec, 1)}
+    return rec
+
+
+def run_once(w):
+    """One call of workload w; its output on the host."""
+    import torch
+    import dense_gemm_fp16_amd as g
+    A, B, C, D = _device_inputs(w, torch)
+    g.gemm_tn(A, B, w.alpha, w.beta, C, out=D)
+    torch.cuda.synchronize()
+    return D.cpu().numpy()
 
 
 def cpu_baseline(w, target_s):
@@ -306,8 +549,9 @@ def cpu_baseline(w, target_s):
                        threads=threads)
         dt = time.perf_counter() - t
     flops = 2.0 * rows * w.N * w.K
+    _, affinity, host = _host_cpus()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
+            "affinity_cpus": affinity, "host_cpus": host, "kind": "oracle",
             "sample": f"first {rows} of {rows_total} rows of D "
                       f"({rows}x{w.N}x{w.K}, fp64 sequential k-sum), "
                       f"{dt:.1f} s on {threads} threads of {_cpu_model()}; "
@@ -548,6 +792,62 @@ def transpose_main(a):
     print(json.dumps(line), flush=True)
 
 
+def extras_table(a):
+    """stderr table of the workloads beyond the study's configurations: the
+    tail-split shape, the attention forward pass, the fp16-accumulating
+    GEMM and the transposes (HIP events, a steps x back-to-back calls)."""
+    import seeded_inputs as si
+    print(f"{'workload':<14}{'kernel':<60}{'us':>10}{'TFLOP/s':>10}"
+          f"{'%peak':>8}{'GB/s':>9}{'%HBM':>7}", file=sys.stderr)
+    for name in si.WORKLOADS:
+        if name in CONFIGS:
+            continue
+        wx = si.workload(name)
+        s = time_workload(wx, a.steps, a.warmup)
+        tf = wx.flops / s / 1e12
+        gb = wx.algorithmic_bytes / s / 1e9
+        print(f"{name:<14}{describe(wx):<60}{s * 1e6:>10.2f}{tf:>10.1f}"
+              f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
+              f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+    for name in ATTENTIONS:
+        wa = si.attention_workload(name)
+        s = time_attention(wa, a.steps, a.warmup)
+        tf = wa.flops / s / 1e12
+        gb = wa.algorithmic_bytes / s / 1e9
+        print(f"{name:<14}{'attention forward, 128 queries x 64 keys':<60}"
+              f"{s * 1e6:>10.2f}{tf:>10.1f}"
+              f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
+              f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+    for name, (batch, M, N, K) in F16ACCS.items():
+        s = time_f16acc(batch, M, N, K, a.steps, a.warmup)
+        tf = 2.0 * batch * M * N * K / s / 1e12
+        gb = 2.0 * batch * (M * K + N * K + M * N) / s / 1e9
+        print(f"{name:<14}{'fp16 accumulation, 128x128x32, k16 MFMA':<60}"
+              f"{s * 1e6:>10.2f}{tf:>10.1f}"
+              f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
+              f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+    for name, (batch, M, N) in TRANSPOSES.items():
+        s = time_transpose(batch, M, N, a.steps, a.warmup)
+        gb = 8.0 * batch * M * N / s / 1e9
+        print(f"{name:<14}{'fp32 transpose, 64x64 tiles':<60}"
+              f"{s * 1e6:>10.2f}{'-':>10}{'-':>8}{gb:>9.0f}"
+              f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
+
+
+def gemm_workload(name):
+    """A workload of the study by name, or `tn_MxNxK`: an M x N x K product
+    of seeded uniform [-1, 1] fp16 operands with fp16 D, alpha 1, beta 0
+    (the 4096^3 recipe at other sizes, for sweeps)."""
+    import re
+    import seeded_inputs as si
+    m = re.fullmatch(r"tn_(\d+)x(\d+)x(\d+)", name)
+    if m is None:
+        return si.workload(name)
+    M, N, K = (int(x) for x in m.groups())
+    return si.build(name, 1, M, N, K, 1.0, 0.0, "f16", "uniform",
+                    si.SEED_BASE + 0x300)
+
+
 def describe(w):
     import dense_gemm_fp16_amd as g
     return g.describe(w.batch, w.M, w.N, w.K, w.beta, w.out_dtype, True)
@@ -557,6 +857,9 @@ def main():
     a = _args()
     if a.summarize_trace:
         print(json.dumps(summarize_trace(a.summarize_trace, a.workload)))
+        return
+    if a.summarize_trace_all:
+        print(summarize_trace_all(*a.summarize_trace_all[:2]))
         return
     if a.summarize_pmc:
         t = summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.workload,
@@ -592,22 +895,17 @@ def main():
     if a.workload in F16ACCS:
         f16acc_main(a)
         return
-    w = si.workload(a.workload)
+    if a.all:
+        # one record per configuration of the study, each with its oracle
+        for name in CONFIGS:
+            print(json.dumps(config_record(name, a.steps, a.warmup,
+                                           cpu=not a.no_cpu_baseline)),
+                  flush=True)
+    if a.extras:
+        extras_table(a)
+    w = gemm_workload(a.workload)
     sec = time_workload(w, a.steps, a.warmup)
-    tflops = w.flops / sec / 1e12
-    gbs = w.algorithmic_bytes / sec / 1e9
-    compute_bound = w.flops / w.algorithmic_bytes > (
-        PEAK_F16_MFMA_TFLOPS * 1e12) / (PEAK_HBM_GBS * 1e9)
-    if compute_bound:
-        roof = {"bound": "mfma", "achieved": round(tflops, 2),
-                "peak": PEAK_F16_MFMA_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(tflops / PEAK_F16_MFMA_TFLOPS, 4)}
-    else:
-        roof = {"bound": "hbm", "achieved": round(gbs, 1),
-                "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                "frac": round(gbs / PEAK_HBM_GBS, 4)}
-    t = load_traffic(a.workload)
-    roof["traffic"] = round(t["bytes_per_launch"]) if t else None
+    tflops, gbs, roof = roofline_of(w, sec, load_traffic(a.workload))
     line = {
         "metric": (f"GEMM TFLOP/s (fp16 in, fp32 acc) at "
                    + ("4096^3" if a.workload == "c3_4096"
@@ -634,40 +932,6 @@ def main():
                    "kernel": describe(w)},
         "roofline": roof,
     }
-    if a.all:
-        print(f"{'workload':<14}{'kernel':<60}{'us':>10}{'TFLOP/s':>10}"
-              f"{'%peak':>8}{'GB/s':>9}{'%HBM':>7}", file=sys.stderr)
-        for name in si.WORKLOADS:
-            wx = si.workload(name)
-            s = time_workload(wx, a.steps, a.warmup)
-            tf = wx.flops / s / 1e12
-            gb = wx.algorithmic_bytes / s / 1e9
-            print(f"{name:<14}{describe(wx):<60}{s * 1e6:>10.2f}{tf:>10.1f}"
-                  f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
-                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
-        for name in ATTENTIONS:
-            wa = si.attention_workload(name)
-            s = time_attention(wa, a.steps, a.warmup)
-            tf = wa.flops / s / 1e12
-            gb = wa.algorithmic_bytes / s / 1e9
-            print(f"{name:<14}{'attention forward, 128 queries x 64 keys':<60}"
-                  f"{s * 1e6:>10.2f}{tf:>10.1f}"
-                  f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
-                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
-        for name, (batch, M, N, K) in F16ACCS.items():
-            s = time_f16acc(batch, M, N, K, a.steps, a.warmup)
-            tf = 2.0 * batch * M * N * K / s / 1e12
-            gb = 2.0 * batch * (M * K + N * K + M * N) / s / 1e9
-            print(f"{name:<14}{'fp16 accumulation, 128x128x32, k16 MFMA':<60}"
-                  f"{s * 1e6:>10.2f}{tf:>10.1f}"
-                  f"{100 * tf / PEAK_F16_MFMA_TFLOPS:>8.2f}{gb:>9.0f}"
-                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
-        for name, (batch, M, N) in TRANSPOSES.items():
-            s = time_transpose(batch, M, N, a.steps, a.warmup)
-            gb = 8.0 * batch * M * N / s / 1e9
-            print(f"{name:<14}{'fp32 transpose, 64x64 tiles':<60}"
-                  f"{s * 1e6:>10.2f}{'-':>10}{'-':>8}{gb:>9.0f}"
-                  f"{100 * gb / PEAK_HBM_GBS:>7.1f}", file=sys.stderr)
     if a.cold:
         cs = time_workload_cold(w, a.steps)
         line["cold"] = {"ms_per_call": round(cs * 1e3, 5),

@@ -170,6 +170,15 @@ def workload(name: str, int_values: bool = False) -> Workload:
                  kind=kind, seed=seed, **cfg)
 
 
+def workload_shape(name: str) -> Workload:
+    """The workload's sizes, alpha, beta and output type, without its data
+    (A, B and C are None): for code that needs only the shape."""
+    cfg = dict(WORKLOADS[name])
+    return Workload(name, cfg["batch"], cfg["M"], cfg["N"], cfg["K"],
+                    cfg["alpha"], cfg["beta"], cfg["out_dtype"], None, None,
+                    None)
+
+
 @dataclass
 class AttentionWorkload:
     """One attention forward problem, O = softmax(scale * Q K^T) V, over

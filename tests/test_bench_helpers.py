@@ -89,3 +89,39 @@ def test_more_than_one_gpu_is_refused():
                        timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_summarize_trace_all_finds_each_configuration(tmp_path):
+    """Each configuration's kernels are picked out of one mixed trace by
+    name, grid and workgroup size; a split-K call adds its reduction; the
+    run's stdout records are set beside the kernel times."""
+    import seeded_inputs as si
+    rows, t = [], 0
+    for i, name in enumerate(bench.CONFIGS):
+        for part, grid, wg in bench.trace_signatures(si.workload_shape(name)):
+            for rep in range(3):
+                dur = 1000 * (i + 1) + 10 * rep + (7 if "reduce" in part
+                                                    else 0)
+                rows.append({"Kernel_Name": f"void gtn::{part}<...>",
+                             "Start_Timestamp": t, "End_Timestamp": t + dur,
+                             "Grid_Size_X": grid, "Workgroup_Size_X": wg})
+                t += dur + 5
+    p = tmp_path / "k_kernel_trace.csv"
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=list(rows[0]))
+        w.writeheader()
+        w.writerows(rows)
+    j = tmp_path / "b.jsonl"
+    j.write_text('{"record": "config", "workload": "c4b_skinny", '
+                 '"us_per_call": 12.5, "cpu_baseline": {"seconds": 0.7, '
+                 '"cores": 16}, "parity": {"float_within_tolerance": true, '
+                 '"integer_bit_exact": true}}\n{"metric": "x"}\n')
+    table = bench.summarize_trace_all(str(p), str(j)).splitlines()
+    assert len(table) == 2 + len(bench.CONFIGS)
+    by = {r.split("|")[1].strip(): r.split("|") for r in table[2:]}
+    # c3, the third configuration: median of 3000, 3010, 3020 ns
+    assert by["c3_4096"][4].strip() == "3.01"
+    # c4b: gemm median 5010 + reduction median 5017
+    assert by["c4b_skinny"][4].strip() == "10.03"
+    assert "12.5" in by["c4b_skinny"][10] and "0.7 (16)" in by["c4b_skinny"][11]
+    assert by["c1_256"][10].strip() == "-"

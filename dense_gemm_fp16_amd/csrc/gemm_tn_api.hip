@@ -139,6 +139,8 @@ int launch_rows(const GemmArgs &a, const Plan &p, int splits, unsigned grid,
                 bool out_f32, hipStream_t s)
 {
     const bool split = splits > 1;
+    if (split && a.ws == nullptr)
+        return GEMM_TN_ERR_WORKSPACE;    // partials need somewhere to go
     hipError_t e;
     switch (p.tile) {
     case TILE_256:

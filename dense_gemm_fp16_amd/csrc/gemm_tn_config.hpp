@@ -28,8 +28,16 @@
 #ifndef GTN_T128_STAGES
 #define GTN_T128_STAGES 2
 #endif
+// The 64 tile takes 128-deep k-tiles (rows of 256 bytes) for whole-K
+// problems, 64-deep ones for split-K slices: measured (kernel trace, one
+// box), 1024^3 with C ran 6.7-7.5 us against 8.0-8.1 us with 64-deep
+// tiles, 1000x1030x1000 and 256^3 the same; the 128x4096x8192 slices
+// gained nothing from 128 (16.6 against 16.4 us).
 #ifndef GTN_T64_BK
-#define GTN_T64_BK 64
+#define GTN_T64_BK 128
+#endif
+#ifndef GTN_T64_SPLIT_BK
+#define GTN_T64_SPLIT_BK 64
 #endif
 // The 64 tile runs short K loops of small problems with a two-stage ring,
 // and split-K slices (long loops, two workgroups per CU) with four stages:

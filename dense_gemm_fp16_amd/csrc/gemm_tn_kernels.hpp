@@ -285,7 +285,7 @@ __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 
 // ---------------------------------------------------------------------------
 // Main kernel.
-//   BM x BN x BK : workgroup tile (BK = 32 or 64); WM x WN waves;
+//   BM x BN x BK : workgroup tile (BK = 32, 64 or 128); WM x WN waves;
 //   STAGES : LDS ring depth of the direct loader (tile t + STAGES - 1 is in
 //            flight while tile t is multiplied);
 //   LOADER : LOAD_DIRECT (16-byte buffer loads straight into LDS),
@@ -334,7 +334,8 @@ gemm_tn_kernel(GemmArgs p)
     constexpr int CHUNKS = BK / 8;            // 16-byte chunks per tile row
     constexpr int ROWS_PER_WAVE_LOAD = 64 / CHUNKS;
     constexpr int STAGE_HALVES = (BM + BN) * BK;
-    static_assert(BK == 32 || BK == 64, "tile rows of 64 or 128 bytes");
+    static_assert(BK == 32 || BK == 64 || BK == 128,
+                  "tile rows of 64, 128 or 256 bytes");
     static_assert(STAGES >= 2, "at least double buffering");
     static_assert(WTM % MB == 0 && WTN % MB == 0, "wave tile of MFMA blocks");
     static_assert(BK % KM == 0, "whole k-steps per tile");

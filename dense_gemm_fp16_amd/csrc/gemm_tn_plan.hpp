@@ -22,9 +22,12 @@ constexpr int kTileDim[NUM_TILES] = {256, 128, 64};
 constexpr int kTileBK[NUM_TILES] = {GTN_T256_BK, GTN_T128_BK, GTN_T64_BK};
 constexpr int kTileStages[NUM_TILES] = {GTN_T256_STAGES, GTN_T128_STAGES,
                                         GTN_T64_STAGES};
-// Ring depth of split-K slices (differs on the 64 tile only).
+// Ring depth and k-tile depth of split-K slices (differ on the 64 tile
+// only).
 constexpr int kTileSplitStages[NUM_TILES] = {
     GTN_T256_STAGES, GTN_T128_STAGES, GTN_T64_SPLIT_STAGES};
+constexpr int kTileSplitBK[NUM_TILES] = {GTN_T256_BK, GTN_T128_BK,
+                                         GTN_T64_SPLIT_BK};
 constexpr int kTileWM[NUM_TILES] = {GTN_T256_WM, 2, 2};
 constexpr int kTileWN[NUM_TILES] = {GTN_T256_WN, 2, 2};
 constexpr int kTileSched[NUM_TILES] = {GTN_T256_SCHED, 0, 0};
@@ -402,7 +405,8 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
              "loader=%s a_along=%s b_along=%s split=%d k_split=%lld "
              "vec_out=%d group_m=%d grid=%lld tail_rows=%d tail_split=%d "
              "tail_k_split=%lld tail_grid=%lld",
-             p.bm, p.bn, kTileBK[p.tile],
+             p.bm, p.bn,
+             p.splits > 1 ? kTileSplitBK[p.tile] : kTileBK[p.tile],
              p.splits > 1 ? kTileSplitStages[p.tile] : kTileStages[p.tile],
              kTileWM[p.tile], kTileWN[p.tile], kTileMfma[p.tile],
              kTileMfma[p.tile],

@@ -9,7 +9,7 @@ hipError_t launch_tile64(const GemmArgs &a, int loader, int layout,
                          unsigned grid, hipStream_t s)
 {
     if (split)
-        return launch_tile<64, 64, GTN_T64_BK, 2, 2, GTN_T64_SPLIT_STAGES, 2,
+        return launch_tile<64, 64, GTN_T64_SPLIT_BK, 2, 2, GTN_T64_SPLIT_STAGES, 2,
                            0, GTN_T64_MFMA, GTN_T64_DIRECT_LAYS,
                            GTN_T64_ELEM_LAYS, KERNELS_SPLIT>(
             a, loader, layout, out_f32, split, vec_out, grid, s);

@@ -329,6 +329,7 @@ int main()
     gemm_tile<128, 128, 64, 2, 2, 32>();
     gemm_tile<64, 64, 64, 2, 2, 32>();
     gemm_tile<128, 128, 32, 2, 2, 16>();
+    gemm_tile<64, 64, 128, 2, 2, 16>();       // 256-byte rows
     // Operands stored along M / N: A (W = BM, a wave's rows at wm * WTM,
     // MI fragments) and B (W = BN, columns at wn * WTN, NI fragments).
     for (int wm = 0; wm < 2; ++wm)
@@ -338,6 +339,7 @@ int main()
     for (int w = 0; w < 2; ++w) {
         mn_tile<128, 64>(w * 64, 4);
         mn_tile<64, 64>(w * 32, 2);
+        mn_tile<64, 128>(w * 32, 2);          // 128 k-rows
     }
     // Epilogue staging: wave sub-tiles of the 256 and 128 tiles (128 x 64,
     // 64 x 64) and the 64 tile (32 x 32), fp16, fp32 and split-K partials.

@@ -193,11 +193,12 @@ def test_plans_for_the_workloads():
     assert p["tile"].startswith("256x256x") and p["split"] == "1"
     assert p["grid"] == "256" and p["loader"] != "elem"
     # 1024^3 and the ragged 1000x1030x1000: 64x64 tiles, enough of them
-    # (whole-K problems on the 64 tile take its two-stage ring)
+    # (whole-K problems on the 64 tile take its two-stage ring of 128-deep
+    # k-tiles)
     p = describe(1, 1024, 1024, 1024, 0.5, "f32")
-    assert p["tile"] == "64x64x64" and p["stages"] == "2"
+    assert p["tile"] == "64x64x128" and p["stages"] == "2"
     p = describe(1, 1000, 1030, 1000, 0.0, "f32")
-    assert p["tile"] == "64x64x64" and p["vec_out"] == "0"   # N % 4 != 0
+    assert p["tile"] == "64x64x128" and p["vec_out"] == "0"   # N % 4 != 0
     assert p["stages"] == "2"
     # skinny 128x4096x8192: split-K, slices on the four-stage ring
     p = describe(1, 128, 4096, 8192, 0.0, "f32")

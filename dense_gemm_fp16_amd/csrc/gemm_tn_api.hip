@@ -223,6 +223,10 @@ int run(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
     a.splits = p.splits;
     a.k_split = (int)p.k_split;
     a.group_m = p.group_m;
+    if (p.onek) {
+        const hipError_t e = launch_onek(a, out_f32, (unsigned)p.grid, s);
+        return e == hipSuccess ? GEMM_TN_OK : GEMM_TN_ERR_LAUNCH;
+    }
     std::unique_lock<std::mutex> ws_lock;   // held until the launches
     if (p.splits > 1 || p.tail_rows > 0) {
         st = noalloc ? get_static_scratch(p.ws_bytes, &a.ws)

@@ -22,6 +22,11 @@ hipError_t launch_tile64(const GemmArgs &a, int loader, int layout,
                          unsigned grid, hipStream_t s);
 hipError_t launch_splitk_reduce(const GemmArgs &a, bool out_f32,
                                 bool vec_out, hipStream_t s);
+// Persistent kernel for K <= 64 (gemm_tn_onek.hip): 128 x 128 tiles walked
+// by `grid` workgroups, the next tile's operands loaded while the current
+// tile's stores drain.
+hipError_t launch_onek(const GemmArgs &a, bool out_f32, unsigned grid,
+                       hipStream_t s);
 
 // Kernels instantiated for a launcher: bit 0 = whole-K kernels, bit 1 =
 // split-K slices (a tile may run the two with different ring depths).

@@ -79,7 +79,13 @@ struct Plan {
     int tail_splits = 1;
     int64_t tail_k_split = 0;
     int64_t tail_grid = 0;
+    // Persistent one-k-tile kernel (K <= kOneK, 128 x 128 tiles, `grid`
+    // workgroups walking tiles_m * tiles_n * batch tiles).
+    bool onek = false;
 };
+
+constexpr int64_t kOneK = 64;           // deepest K the one-k-tile kernel takes
+constexpr int64_t kOneKMinTiles = 512;  // fewer tiles: one per workgroup
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
@@ -171,12 +177,13 @@ inline int check_pointers(int64_t M, int64_t N, int64_t K, const void *A,
 }
 
 // Optional override for tuning sweeps and tests: "tile=256|128|64,
-// loader=0|1|2,split=S,group=G,tail=R,tail_split=T" (any subset, comma
-// separated; tail=0 turns the tail split off).  Unknown keys are ignored;
+// loader=0|1|2,split=S,group=G,tail=R,tail_split=T,onek=0|1" (any subset,
+// comma separated; tail=0 turns the tail split off; onek=1 takes the
+// persistent one-k-tile kernel wherever it applies, onek=0 never).  Unknown keys are ignored;
 // a loader that the operands' alignment does not allow is ignored.
 struct Override {
     int tile = -1, loader = -1, split = -1, group = -1, tail = -1,
-        tail_split = -1;
+        tail_split = -1, onek = -1;
 };
 
 inline Override parse_override(const char *s)
@@ -208,6 +215,8 @@ inline Override parse_override(const char *s)
             o.tail = v >= 0 ? v : -1;
         else if (!strcmp(tok, "tail_split"))
             o.tail_split = v >= 2 ? v : -1;
+        else if (!strcmp(tok, "onek"))
+            o.onek = v == 0 || v == 1 ? v : -1;
     }
     return o;
 }
@@ -270,6 +279,31 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         tile = o.tile >= 0 ? o.tile : tile;
         while (!has_kernel(tile) && tile + 1 < NUM_TILES)
             ++tile;
+    }
+    // K within one k-tile, many tiles, 16-byte loads and stores: the
+    // persistent one-k-tile kernel (128 x 128 tiles), which keeps the next
+    // tile's operands in flight while a tile's results are written.
+    {
+        const int64_t t128 = tiles(TILE_128);
+        const bool able = K > 0 && K <= kOneK && layout == 0 &&
+                          loader == PLAN_LOAD_DIRECT && vec_out &&
+                          o.split < 2 && o.tail < 1;
+        const bool want = o.onek >= 0 ? o.onek == 1
+                                      : o.tile < 0 && t128 >= kOneKMinTiles;
+        if (able && want) {
+            p.onek = true;
+            p.tile = TILE_128;
+            p.bm = p.bn = 128;
+            p.loader = loader;
+            p.vec_out = true;
+            p.tiles_m = (int)cdiv(M, 128);
+            p.tiles_n = (int)cdiv(N, 128);
+            p.splits = 1;
+            p.k_split = kBK;
+            p.group_m = 1;
+            p.grid = t128 < kCUs ? t128 : kCUs;
+            return p;
+        }
     }
     p.tile = tile;
     p.bm = p.bn = kTileDim[tile];
@@ -398,6 +432,15 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
     }
     if (p.noop) {
         snprintf(buf, (size_t)buflen, "noop");
+        return p.status;
+    }
+    if (p.onek) {
+        snprintf(buf, (size_t)buflen,
+                 "tile=128x128x64 stages=2 waves=2x2 mfma=16x16 "
+                 "sched=persistent-onek loader=direct a_along=k b_along=k "
+                 "split=1 k_split=64 vec_out=1 group_m=1 grid=%lld "
+                 "tail_rows=0 tail_split=1 tail_k_split=0 tail_grid=0",
+                 (long long)p.grid);
         return p.status;
     }
     snprintf(buf, (size_t)buflen,

@@ -205,9 +205,17 @@ def test_plans_for_the_workloads():
     assert int(p["split"]) > 1 and int(p["k_split"]) % 64 == 0
     assert p["tile"] == "64x64x64" and p["stages"] == "4"
     assert int(p["split"]) * int(p["k_split"]) >= 8192
-    # batched QK^T: 64 x (1024 x 1024 x 64)
+    # batched QK^T: 64 x (1024 x 1024 x 64): K within one k-tile, 4096
+    # tiles of 128 walked by one persistent workgroup per CU
     p = describe(64, 1024, 1024, 64, 0.0, "f32")
-    assert p["tile"].startswith("128x128x") and int(p["grid"]) == 64 * 64
+    assert p["tile"].startswith("128x128x") and int(p["grid"]) == 256
+    assert p["sched"] == "persistent-onek"
+    # too few tiles, C rows off 16 bytes, or K past one k-tile: not it
+    assert describe(1, 1024, 1024, 64)["sched"] != "persistent-onek"
+    assert describe(64, 1024, 1030, 64, 0.0, "f32")["sched"] != \
+        "persistent-onek"
+    assert describe(64, 1024, 1024, 72, 0.0, "f32")["sched"] != \
+        "persistent-onek"
     # K not a multiple of 8, or misaligned: element loader
     assert describe(1, 100, 100, 33)["loader"] == "elem"
     assert describe(1, 128, 128, 64, aligned=False)["loader"] == "elem"

@@ -736,3 +736,36 @@ def test_signed_zero_bit_exact(spec, monkeypatch):
                 assert zeros > 50
                 res = oracle.check_exact(D.cpu().numpy(), ref, out)
                 assert res.ok, f"{spec} {out} a={alpha} b={beta}: {res}"
+
+
+ONEK_SHAPES = [(1, 300, 260, 64), (3, 129, 250, 8), (2, 1024, 1024, 64),
+               (1, 4000, 136, 24), (5, 64, 64, 40), (1, 1, 1, 8)]
+
+
+@pytest.mark.parametrize("out", ["f16", "f32"])
+def test_onek_kernel_bit_exact(out, monkeypatch):
+    """The persistent kernel for K <= 64 (a workgroup walks a run of tiles,
+    loading the next tile's operands while the current one's results are
+    written) forced onto ragged shapes: M and N tails, K below one
+    k-tile, batches, fewer tiles than XCDs, with and without C."""
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", "onek=1")
+    for i, (batch, M, N, K) in enumerate(ONEK_SHAPES):
+        beta = -0.5 if i % 2 else 0.0
+        w = _int_workload(batch, M, N, K, out, alpha=1.5, beta=beta)
+        desc = g.describe(batch, M, N, K, beta, out)
+        # 16-byte output rows: N a multiple of 8 (fp16) or 4 (fp32)
+        if (N * (2 if out == "f16" else 4)) % 16:
+            assert "persistent-onek" not in desc, desc
+            continue
+        assert "persistent-onek" in desc, desc
+        _say(f"[onek] {batch}x{M}x{N}x{K} {out} beta={beta}: {desc}")
+        d = run_gpu(w)
+        ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+        res = oracle.check_exact(d, ref, out)
+        assert res.ok, f"{batch}x{M}x{N}x{K} {out}: {res}"
+
+
+def test_onek_kernel_is_planned_for_the_score_product():
+    g = _gpu()
+    assert "persistent-onek" in g.describe(64, 1024, 1024, 64, 0.0, "f32")

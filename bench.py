@@ -46,7 +46,7 @@ CSRC = os.path.join(ROOT, "dense_gemm_fp16_amd", "csrc")
 KERNEL_SOURCES = ("gemm_tn_kernels.hpp", "gemm_tn_config.hpp",
                   "gemm_tn_launch.hpp", "gemm_tn_tile256.hip",
                   "gemm_tn_tile128.hip", "gemm_tn_tile64.hip",
-                  "lds_layout.hpp")
+                  "gemm_tn_onek.hip", "lds_layout.hpp")
 TRANSPOSE_SOURCES = ("transpose.hip", "lds_layout.hpp")
 ATTENTION_SOURCES = ("attention_fwd.hip", "gemm_tn_kernels.hpp",
                      "gemm_tn_config.hpp", "lds_layout.hpp")
@@ -78,7 +78,7 @@ def _kernel_names(workload: str):
         return ("attn_fwd_kernel",)
     if workload in F16ACCS:
         return ("gemm_f16acc_kernel",)
-    return ("gemm_tn_kernel", "splitk_reduce")
+    return ("gemm_tn_kernel", "gemm_onek_kernel", "splitk_reduce")
 
 
 def _code_only(text: str) -> str:
@@ -200,6 +200,10 @@ def _args():
                     help="also time the GEMM with cold caches: a 512 MiB "
                          "write before every launch evicts the operands "
                          "from the L2s and the Infinity Cache")
+    ap.add_argument("--vendor", action="store_true",
+                    help="also time torch.matmul (the vendor BLAS) on the "
+                         "same inputs, interleaved with this library "
+                         "(context only; plain products)")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="median / min / max kernel time per call of "
                          "--workload from a rocprofv3 kernel_trace.csv")
@@ -270,6 +274,40 @@ def time_workload_graph(w, steps, warmup):
     return start.elapsed_time(stop) / 1e3 / steps
 
 
+def time_vendor_interleaved(w, rounds=6, burst=10):
+    """Context, not a target: median time per call (seconds) of this library
+    and of torch.matmul (the vendor BLAS) on the same device inputs, in
+    interleaved bursts of `burst` back-to-back calls, HIP events around each
+    burst.  Only for plain products (alpha 1, beta 0)."""
+    import statistics
+    import torch
+    import dense_gemm_fp16_amd as g
+    A, B, C, D = _device_inputs(w, torch)
+    ours = lambda: g.gemm_tn(A, B, out=D)
+    if w.batch == 1:        # one 2-D product, B passed as a transposed view
+        A2, Bt, V = A[0], B[0].t(), torch.empty_like(D[0])
+    else:                   # batched: a contiguous transposed copy of B
+        A2, Bt, V = A, B.transpose(-1, -2).contiguous(), torch.empty_like(D)
+    if D.dtype == torch.float16:
+        vendor = lambda: torch.matmul(A2, Bt, out=V)
+    else:   # fp16 product with fp32 output: the BLAS call plus a cast
+        vendor = lambda: V.copy_(torch.matmul(A2, Bt))
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    times = {"library": [], "torch_matmul": []}
+    for _ in range(rounds):
+        for name, f in (("library", ours), ("torch_matmul", vendor)):
+            f()
+            f()
+            start.record()
+            for _ in range(burst):
+                f()
+            stop.record()
+            torch.cuda.synchronize()
+            times[name].append(start.elapsed_time(stop) / 1e3 / burst)
+    return {k: statistics.median(v) for k, v in times.items()}
+
+
 def time_workload_cold(w, steps):
     """Median time of one call (seconds) with cold caches: before each
     launch a 512 MiB fill (more than the 256 MB Infinity Cache and the
@@ -326,8 +364,11 @@ def trace_signatures(w):
     """(kernel name part, Grid_Size_X, Workgroup_Size_X) of every kernel one
     call of workload w launches, from the plan describe() reports: the tile
     kernel (512 threads on the 256 tile, 256 on the others), the split-K
-    reduction, and for a tail split the tail rows' kernel and reduction."""
+    reduction, and for a tail split the tail rows' kernel and reduction.
+    A problem within one k-tile runs the persistent one-k kernel alone."""
     kv = dict(x.split("=", 1) for x in describe(w).split())
+    if kv.get("sched") == "persistent-onek":
+        return [("gemm_onek_kernel", int(kv["grid"]) * 256, 256)]
     bm = int(kv["tile"].split("x")[0])
     wg = 512 if bm == 256 else 256
 
@@ -937,6 +978,12 @@ def main():
         line["cold"] = {"ms_per_call": round(cs * 1e3, 5),
                         "tflops": round(w.flops / cs / 1e12, 2),
                         "flush_mib": 512}
+    if a.vendor and w.alpha == 1.0 and w.beta == 0.0:
+        v = time_vendor_interleaved(w)
+        line["vendor_context"] = {
+            "us_per_call": {k: round(t * 1e6, 2) for k, t in v.items()},
+            "tflops": {k: round(w.flops / t / 1e12, 1) for k, t in v.items()},
+            "method": "6 interleaved bursts of 10 calls, medians"}
     if not a.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, a.cpu_seconds)
     print(json.dumps(line), flush=True)

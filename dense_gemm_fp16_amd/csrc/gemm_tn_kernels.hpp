@@ -728,7 +728,13 @@ gemm_tn_kernel(GemmArgs p)
                     issue_part(0, k_begin, lw, 0, A_GROUPS);
                     issue_part(1, k_begin + BK, lw, 0, A_GROUPS);
                 }
-                wait_vmcnt<0>();
+                // Tile 0 is all the first barrier must publish: A(1) may
+                // stay in flight (group 1's wait at the end of its first
+                // load phase covers it before tile 1 is read).
+                if (grp == 1)
+                    wait_vmcnt<A_GROUPS>();
+                else
+                    wait_vmcnt<0>();
                 block_sync();
                 if (grp == 1)
                     block_sync();

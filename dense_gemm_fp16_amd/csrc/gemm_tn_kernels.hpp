@@ -759,12 +759,12 @@ gemm_tn_kernel(GemmArgs p)
                 if (grp == 1)
                     wait_vmcnt<A_GROUPS>();
                 block_sync();
-                // compute phase
-                __builtin_amdgcn_s_setprio(1);
+                // compute phase, at the waves' common priority: raising
+                // the multiplying wave's priority cost 8k cycles per
+                // launch at 4096 x 4096 x 8192 (counters, one box)
 #pragma unroll
                 for (int ks = 0; ks < KSTEPS; ++ks)
                     mma(fa[ks], fb[ks]);
-                __builtin_amdgcn_s_setprio(0);
                 if (grp == 0)
                     wait_vmcnt<0>();
                 block_sync();

@@ -126,10 +126,13 @@ def describe(batch, M, N, K, beta=0.0, out_dtype="f16", aligned16=True,
     return buf.value.decode()
 
 
+_F16, _F32 = torch.float16, torch.float32
+
+
 def _dtype_code(dt) -> int:
-    if dt == torch.float16:
+    if dt is _F16:
         return GEMM_TN_F16
-    if dt == torch.float32:
+    if dt is _F32:
         return GEMM_TN_F32
     raise TypeError("C / D must be float16 or float32")
 
@@ -144,40 +147,42 @@ def _stream_handle(stream, t):
     if stream is not None:
         return stream.cuda_stream
     if _raw_stream is not None:
-        return _raw_stream(t.device.index)
+        return _raw_stream(t.get_device())
     return torch.cuda.current_stream(t.device).cuda_stream
 
 
+# Each helper reads a tensor's shape and strides once: on small problems the
+# Python attribute reads are a visible share of a call.
+
 def _operand(t, name):
-    """(layout, row stride) of a 2-D operand or of each matrix of a batch:
-    unit stride along K, else unit stride along M / N."""
-    if t.dtype != torch.float16:
+    """(layout, row stride, batch stride) of a 2-D operand or of each
+    matrix of a 3-D batch: unit stride along K, else unit stride along
+    M / N."""
+    if t.dtype is not _F16:
         raise TypeError(f"{name} must be float16")
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    rows, k = t.shape[-2], t.shape[-1]
-    if k <= 1 or t.stride(-1) == 1:
-        return GEMM_TN_ROW_K, _ld(t)
-    if rows <= 1 or t.stride(-2) == 1:
-        return GEMM_TN_ROW_MN, t.stride(-1) if k > 1 else max(rows, 1)
+    sh, st = t.shape, t.stride()
+    rows, k = sh[-2], sh[-1]
+    bs = st[0] if len(sh) == 3 else 0
+    if k <= 1 or st[-1] == 1:
+        return GEMM_TN_ROW_K, (st[-2] if rows > 1 else max(k, 1)), bs
+    if rows <= 1 or st[-2] == 1:
+        return GEMM_TN_ROW_MN, st[-1], bs
     raise ValueError(f"{name} needs unit stride along its last or "
                      "second-to-last dimension")
 
 
-def _check_layout(t, name):
+def _matrix(t, name):
+    """(row stride, batch stride) of a row-major C / D (unit element
+    stride along N)."""
     if not t.is_cuda:
         raise ValueError(f"{name} must be on the GPU")
-    if t.dim() and t.shape[-1] > 1 and t.stride(-1) != 1:
+    sh, st = t.shape, t.stride()
+    if sh and sh[-1] > 1 and st[-1] != 1:
         raise ValueError(f"{name} must be row-major with unit element stride")
-
-
-def _ld(t):
-    """Row stride of a 2-D matrix or of each matrix of a 3-D batch."""
-    return t.stride(-2) if t.shape[-2] > 1 else max(t.shape[-1], 1)
-
-
-def _bstride(t):
-    return t.stride(0) if t.dim() == 3 else 0
+    return (st[-2] if sh[-2] > 1 else max(sh[-1], 1),
+            st[0] if len(sh) == 3 else 0)
 
 
 def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
@@ -186,44 +191,43 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
 
     `out` may be given (it is then D and is returned); otherwise D is
     allocated with `out_dtype` (default: C's dtype, else float16)."""
-    layout_a, lda = _operand(A, "A")
-    layout_b, ldb = _operand(B, "B")
-    if A.dim() != B.dim() or A.dim() not in (2, 3):
+    layout_a, lda, sa = _operand(A, "A")
+    layout_b, ldb, sb = _operand(B, "B")
+    ash, bsh = A.shape, B.shape
+    if len(ash) != len(bsh) or len(ash) not in (2, 3):
         raise ValueError("A and B must both be 2-D or both 3-D")
-    batched = A.dim() == 3
-    if batched:
-        batch, M, K = A.shape
-        if B.shape[0] != batch or B.shape[2] != K:
+    if len(ash) == 3:
+        batch, M, K = ash
+        if bsh[0] != batch or bsh[2] != K:
             raise ValueError("B must be (batch, N, K)")
-        N = B.shape[1]
+        N = bsh[1]
         shape = (batch, M, N)
     else:
-        M, K = A.shape
-        if B.shape[1] != K:
+        M, K = ash
+        if bsh[1] != K:
             raise ValueError("B must be (N, K)")
-        N = B.shape[0]
+        N = bsh[0]
         batch, shape = 1, (M, N)
     if out is None:
         dt = out_dtype if out_dtype is not None else (
-            C.dtype if C is not None else torch.float16)
+            C.dtype if C is not None else _F16)
         out = torch.empty(shape, dtype=dt, device=A.device)
-    if tuple(out.shape) != shape:
+    if out.shape != shape:
         raise ValueError(f"out must have shape {shape}")
-    _check_layout(out, "out")
+    ldd, sd = _matrix(out, "out")
     code = _dtype_code(out.dtype)
     c_ptr, ldc, sc = None, N, 0
     if beta != 0.0:
         if C is None:
             raise ValueError("beta != 0 needs C")
-        if tuple(C.shape) != shape or C.dtype != out.dtype:
+        if C.shape != shape or C.dtype is not out.dtype:
             raise ValueError("C must match D's shape and dtype")
-        _check_layout(C, "C")
-        c_ptr, ldc, sc = C.data_ptr(), _ld(C), _bstride(C)
+        ldc, sc = _matrix(C, "C")
+        c_ptr = C.data_ptr()
     st = _lib.gemm_tn_ex(
-        batch, M, N, K, float(alpha), A.data_ptr(), layout_a, lda,
-        _bstride(A), B.data_ptr(), layout_b, ldb, _bstride(B), float(beta),
-        c_ptr, ldc, sc, out.data_ptr(), _ld(out), _bstride(out), code,
-        _stream_handle(stream, out))
+        batch, M, N, K, float(alpha), A.data_ptr(), layout_a, lda, sa,
+        B.data_ptr(), layout_b, ldb, sb, float(beta), c_ptr, ldc, sc,
+        out.data_ptr(), ldd, sd, code, _stream_handle(stream, out))
     if st != OK:
         raise GemmError(st)
     return out

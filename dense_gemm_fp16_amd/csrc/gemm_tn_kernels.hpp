@@ -242,10 +242,26 @@ __device__ inline float load_out_elem(__amdgpu_buffer_rsrc_t r, uint32_t off,
     uint32_t v = __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
     return __builtin_bit_cast(float, v);
 }
+// fp32 -> fp16, round to nearest even, of a value the compiler may not fold
+// into the instruction that produced it.  Left alone, hipcc selects
+// (_Float16)(x * alpha) as a mixed-precision FMA with a +0 addend
+// (v_fma_mixlo_f16 d, alpha, x, 0), and -0 + +0 is +0: a product of -0
+// (alpha < 0 times an exactly cancelling sum) came out as +0 at one
+// accumulator of every 256-tile wave.  The empty asm makes the value opaque.
+__device__ inline _Float16 to_half(float x)
+{
+    asm("" : "+v"(x));
+    return (_Float16)x;
+}
+__device__ inline half4 to_half4(f32x4 v)
+{
+    return half4{to_half(v[0]), to_half(v[1]), to_half(v[2]), to_half(v[3])};
+}
+
 __device__ inline void store_out_elem(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                       float v, _Float16 *)
 {
-    _Float16 h = (_Float16)v;
+    _Float16 h = to_half(v);
     __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, h), r,
                                           off, 0, 0);
 }
@@ -271,8 +287,7 @@ __device__ inline f32x4 load_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
                                       f32x4 v, _Float16 *)
 {
-    half4 h = {(_Float16)v[0], (_Float16)v[1], (_Float16)v[2],
-               (_Float16)v[3]};
+    half4 h = to_half4(v);
     __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h), r,
                                           off, 0, 0);
 }
@@ -963,8 +978,7 @@ gemm_tn_kernel(GemmArgs p)
                     if (ES == 4) {
                         *(f32x4 *)dst = v;
                     } else {
-                        half4 h = {(_Float16)v[0], (_Float16)v[1],
-                                   (_Float16)v[2], (_Float16)v[3]};
+                        half4 h = to_half4(v);
                         *(half4 *)dst = h;
                     }
                 }

@@ -216,8 +216,7 @@ __global__ void __launch_bounds__(256) gemm_onek_kernel(GemmArgs p)
                 if constexpr (ES == 4) {
                     *(f32x4 *)dst = v;
                 } else {
-                    const half4 h = {(_Float16)v[0], (_Float16)v[1],
-                                     (_Float16)v[2], (_Float16)v[3]};
+                    const half4 h = to_half4(v);
                     *(half4 *)dst = h;
                 }
             }

@@ -738,6 +738,58 @@ def test_signed_zero_bit_exact(spec, monkeypatch):
                 assert res.ok, f"{spec} {out} a={alpha} b={beta}: {res}"
 
 
+def _cancelling_problem(batch, M, N, K, seed):
+    """Integer A = [X, X] and B = [Y, -Y] (halves along K): every output is
+    an exact zero, reached from the nonzero partial sum X Y^T of the first
+    half, and an exact zero at every position of every wave's sub-tile.
+    (N a multiple of 8 keeps fp16 rows 16-byte aligned: the staged
+    epilogue with 16-byte stores.)"""
+    r = np.random.default_rng(seed)
+    vals = np.array([-3, -2, -1, 1, 2, 3])
+    X = r.choice(vals, (batch, M, K // 2))
+    Y = r.choice(vals, (batch, N, K // 2))
+    A = np.concatenate([X, X], axis=2).astype(np.float16)
+    B = np.concatenate([Y, -Y], axis=2).astype(np.float16)
+    return A, B
+
+
+CANCEL_CASES = ([(spec, (1, 300, 296, 520)) for spec in
+                 ["", "tile=256,tail=1,tail_split=2",
+                  "tile=64,tail=1,tail_split=3"] + CONFIGS]
+                + [("onek=1", (2, 300, 296, 64)), ("onek=0", (2, 300, 296, 64))])
+
+
+@pytest.mark.parametrize("spec,shape", CANCEL_CASES)
+def test_cancelling_sums_keep_the_sign_of_zero(spec, shape, monkeypatch):
+    """alpha * (an exactly cancelling sum) is alpha * (+0): -0 for negative
+    alpha, at every output position, fp16 and fp32, with and without a
+    beta term on zeros of both signs.  Regression: hipcc selected the fp16
+    epilogue's (half)(x * alpha) of one accumulator per 256-tile wave as a
+    mixed FMA with a +0 addend, which gave +0 where -0 is the result."""
+    g = _gpu()
+    if spec:
+        monkeypatch.setenv("GEMM_TN_FORCE", spec)
+    batch, M, N, K = shape
+    A, B = _cancelling_problem(batch, M, N, K, 0x5EED0C0 + K)
+    At, Bt = torch.from_numpy(A).cuda(), torch.from_numpy(B).cuda()
+    r = np.random.default_rng(0x5EED0C1)
+    for out in ("f16", "f32"):
+        dt = np.float16 if out == "f16" else np.float32
+        C = np.where(r.integers(0, 2, (batch, M, N)) == 1, dt(-0.0), dt(0.0))
+        Ct = torch.from_numpy(C).cuda()
+        for alpha in (1.0, -1.5):
+            for beta in (0.0, 0.5):
+                _say(f"[cancelling] {spec or 'planner'} {shape} out={out} "
+                     f"alpha={alpha} beta={beta}")
+                D = g.gemm_tn(At, Bt, alpha, beta, Ct if beta else None,
+                              out_dtype=_dt(out))
+                torch.cuda.synchronize()
+                ref = oracle.gemm_tn(A, B, alpha, beta, C if beta else None)
+                assert not ref.any()
+                res = oracle.check_exact(D.cpu().numpy(), ref, out)
+                assert res.ok, f"{spec} {out} a={alpha} b={beta}: {res}"
+
+
 ONEK_SHAPES = [(1, 300, 260, 64), (3, 129, 250, 8), (2, 1024, 1024, 64),
                (1, 4000, 136, 24), (5, 64, 64, 40), (1, 1, 1, 8)]
 

@@ -1098,40 +1098,36 @@ gemm_tn_kernel(GemmArgs p)
         return;
     }
 
-    // With C: element by element, straight from the accumulators.
-    auto store_all = [&](auto with_c) {
-        constexpr bool WITH_C = decltype(with_c)::value;
+    // With C (beta != 0 here): element by element, straight from the
+    // accumulators.  The value converted is fma(beta, c, alpha * acc), not a
+    // bare product, so it takes the plain conversion: to_half's asm would
+    // hold every value in its own register, and on the 256 tile that spills.
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i)
 #pragma unroll
-            for (int j = 0; j < NI; ++j)
+        for (int j = 0; j < NI; ++j)
 #pragma unroll
-                for (int g = 0; g < G; ++g) {
-                    const int lm = wm * WTM + i * MB + em;
-                    const int64_t n = n0 + wn * WTN + j * MB + 4 * QN * g + en;
+            for (int g = 0; g < G; ++g) {
+                const int lm = wm * WTM + i * MB + em;
+                const int64_t n = n0 + wn * WTN + j * MB + 4 * QN * g + en;
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const bool in = n + e < N;
-                        const uint32_t offd =
-                            in ? (uint32_t)((lm * ldd + n + e) * ES)
-                               : kOutOfRange;
-                        float x = acc[i][j][4 * g + e] * alpha;
-                        if (WITH_C) {
-                            const uint32_t offc =
-                                in ? (uint32_t)((lm * ldc + n + e) * ES)
-                                   : kOutOfRange;
-                            x = __builtin_fmaf(
-                                beta, load_out_elem(rC, offc, (OutT *)nullptr),
-                                x);
-                        }
+                for (int e = 0; e < 4; ++e) {
+                    const bool in = n + e < N;
+                    const uint32_t offd =
+                        in ? (uint32_t)((lm * ldd + n + e) * ES) : kOutOfRange;
+                    const uint32_t offc =
+                        in ? (uint32_t)((lm * ldc + n + e) * ES) : kOutOfRange;
+                    const float x = __builtin_fmaf(
+                        beta, load_out_elem(rC, offc, (OutT *)nullptr),
+                        acc[i][j][4 * g + e] * alpha);
+                    if constexpr (ES == 2)
+                        __builtin_amdgcn_raw_buffer_store_b16(
+                            __builtin_bit_cast(uint16_t, (_Float16)x), rD,
+                            offd, 0, 0);
+                    else
                         store_out_elem(rD, offd, x, (OutT *)nullptr);
-                    }
                 }
-    };
-    if (use_c)
-        store_all(Bool<true>{});
-    else
-        store_all(Bool<false>{});
+            }
 }
 
 // ---------------------------------------------------------------------------

@@ -83,6 +83,23 @@ _lib.gemm_tn_status_string.argtypes = [_int]
 _lib.gemm_tn_version.restype = _int
 _lib.gemm_tn_version.argtypes = []
 
+# The fast path of gemm_tn() (csrc/binding_fast.cpp): the same marshalling
+# in C++ against torch's tensor API, calling this library's gemm_tn_ex
+# through the pointer handed over here.  Without it (not built, or built
+# for another torch) the calls are marshalled through ctypes.
+_fast = None
+_FAST_PATH = os.path.join(_HERE, "_gemm_tn_fast.so")
+if os.path.exists(_FAST_PATH):
+    import importlib.util as _ilu
+    try:
+        _spec = _ilu.spec_from_file_location(__name__ + "._gemm_tn_fast",
+                                             _FAST_PATH)
+        _fast = _ilu.module_from_spec(_spec)
+        _spec.loader.exec_module(_fast)
+        _fast.set_entry(ctypes.cast(_lib.gemm_tn_ex, ctypes.c_void_p).value)
+    except ImportError:
+        _fast = None
+
 
 
 class GemmError(RuntimeError):
@@ -185,12 +202,46 @@ def _matrix(t, name):
             st[0] if len(sh) == 3 else 0)
 
 
+def _out_shape(A, B):
+    ash, bsh = A.shape, B.shape
+    if len(ash) != len(bsh) or len(ash) not in (2, 3):
+        raise ValueError("A and B must both be 2-D or both 3-D")
+    if len(ash) == 3:
+        if bsh[0] != ash[0] or bsh[2] != ash[2]:
+            raise ValueError("B must be (batch, N, K)")
+        return (ash[0], ash[1], bsh[1])
+    if bsh[1] != ash[1]:
+        raise ValueError("B must be (N, K)")
+    return (ash[0], bsh[0])
+
+
 def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
             out_dtype=None, stream=None):
     """D = alpha * A @ B^T + beta * C on the GPU (2-D or batched 3-D).
 
     `out` may be given (it is then D and is returned); otherwise D is
     allocated with `out_dtype` (default: C's dtype, else float16)."""
+    if out is None:
+        dt = out_dtype if out_dtype is not None else (
+            C.dtype if C is not None else _F16)
+        out = torch.empty(_out_shape(A, B), dtype=dt, device=A.device)
+    if _fast is not None and out.is_cuda:
+        try:
+            st = _fast.gemm_tn_fast(A, B, out, alpha, beta,
+                                    C if beta != 0.0 else None,
+                                    _stream_handle(stream, out))
+        except TypeError:      # not tensors / numbers: the checked path says
+            st = -1
+        if st == OK:
+            return out
+        if st > 0:
+            raise GemmError(st)
+    return _gemm_tn_checked(A, B, alpha, beta, C, out, stream)
+
+
+def _gemm_tn_checked(A, B, alpha, beta, C, out, stream):
+    """gemm_tn() with every argument checked in Python (the path for calls
+    the fast path hands back, and without it)."""
     layout_a, lda, sa = _operand(A, "A")
     layout_b, ldb, sb = _operand(B, "B")
     ash, bsh = A.shape, B.shape
@@ -208,10 +259,6 @@ def gemm_tn(A, B, alpha: float = 1.0, beta: float = 0.0, C=None, out=None,
             raise ValueError("B must be (N, K)")
         N = bsh[0]
         batch, shape = 1, (M, N)
-    if out is None:
-        dt = out_dtype if out_dtype is not None else (
-            C.dtype if C is not None else _F16)
-        out = torch.empty(shape, dtype=dt, device=A.device)
     if out.shape != shape:
         raise ValueError(f"out must have shape {shape}")
     ldd, sd = _matrix(out, "out")

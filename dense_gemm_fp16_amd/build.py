@@ -89,6 +89,32 @@ def build(defines=(), out_path=LIB_PATH, jobs=None, save_temps=False) -> str:
     return out_path
 
 
+FAST_NAME = "_gemm_tn_fast"
+FAST_PATH = os.path.join(PKG, FAST_NAME + ".so")
+
+
+def build_fast_binding() -> str:
+    """The binding's fast path (csrc/binding_fast.cpp, host C++ against
+    torch's headers, no HIP): built with torch.utils.cpp_extension into
+    _build/, then placed next to the library.  The package imports it when
+    present and otherwise marshals through ctypes."""
+    import shutil
+    from torch.utils import cpp_extension
+    bdir = os.path.join(BUILD_DIR, "fast_binding")
+    os.makedirs(bdir, exist_ok=True)
+    cpp_extension.load(name=FAST_NAME,
+                       sources=[os.path.join(CSRC, "binding_fast.cpp")],
+                       extra_cflags=["-O2", "-I" + os.path.join(ROOT,
+                                                                "include")],
+                       build_directory=bdir, with_cuda=False,
+                       is_python_module=True, verbose=False)
+    built = os.path.join(bdir, FAST_NAME + ".so")
+    tmp = FAST_PATH + ".tmp%d" % os.getpid()
+    shutil.copyfile(built, tmp)
+    os.replace(tmp, FAST_PATH)
+    return FAST_PATH
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--defines", nargs="*", default=[])

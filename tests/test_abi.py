@@ -366,3 +366,22 @@ def test_noalloc_rejects_plans_beyond_its_scratch():
     # argument errors are still reported first
     assert g.gemm_tn_ex_noalloc(1, -1, N, K, 1.0, P, K, 0, P, K, 0, 0.0, NULL,
                                 N, 0, P, N, 0, F32, S) == INVALID
+
+
+def test_fast_binding_is_loaded_and_hands_back_what_it_does_not_take():
+    """The binding's C++ fast path is built next to the library and loaded;
+    it returns -1 (leaving the call to the checked Python path) for every
+    call outside the plain cases, before touching a device."""
+    torch = pytest.importorskip("torch")
+    assert g._fast is not None, "fast binding not built (build())"
+    h = torch.float16
+    A = torch.zeros(4, 8, dtype=h)
+    B = torch.zeros(5, 8, dtype=h)
+    D = torch.zeros(4, 5, dtype=h)
+    f = g._fast.gemm_tn_fast
+    assert f(A, B, D, 1.0, 0.0, None, 0) == -1          # host tensors
+    assert f(A.float(), B, D, 1.0, 0.0, None, 0) == -1  # A not fp16
+    assert f(A, B[:, :4], D, 1.0, 0.0, None, 0) == -1   # K mismatch
+    assert f(A, B, D, 1.0, 0.5, None, 0) == -1          # beta without C
+    with pytest.raises(ValueError, match="on the GPU"):
+        g.gemm_tn(A, B, out=D)                          # checked path

@@ -365,25 +365,29 @@ def summarize_trace(csv_path, workload):
 def trace_signatures(w):
     """(kernel name part, Grid_Size_X, Workgroup_Size_X) of every kernel one
     call of workload w launches, from the plan describe() reports: the tile
-    kernel (512 threads on the 256 tile, 256 on the others), the split-K
+    kernel (64 threads per wave of the plan's waves), the split-K
     reduction, and for a tail split the tail rows' kernel and reduction.
     A problem within one k-tile runs the persistent one-k kernel alone."""
     kv = dict(x.split("=", 1) for x in describe(w).split())
     if kv.get("sched") == "persistent-onek":
         return [("gemm_onek_kernel", int(kv["grid"]) * 256, 256)]
     bm = int(kv["tile"].split("x")[0])
-    wg = 512 if bm == 256 else 256
+    wm, wn = (int(x) for x in kv["waves"].split("x"))
+    wg = 64 * wm * wn
 
     def reduce_sig(rows):
         work = w.batch * rows * ((w.N + 3) // 4)
         return ("splitk_reduce", (work + 255) // 256 * 256, 256)
 
-    sigs = [("gemm_tn_kernel", int(kv["grid"]) * wg, wg)]
+    # the tile's edge is in the (mangled) kernel name: launches of two tiles
+    # may agree in grid and workgroup size (256 workgroups of 256 threads)
+    part = f"gemm_tn_kernelILi{bm}ELi{bm}E"
+    sigs = [(part, int(kv["grid"]) * wg, wg)]
     if int(kv["split"]) > 1:
         sigs.append(reduce_sig(w.M))
     tail_rows = int(kv["tail_rows"])
     if tail_rows > 0:
-        sigs.append(("gemm_tn_kernel", int(kv["tail_grid"]) * wg, wg))
+        sigs.append((part, int(kv["tail_grid"]) * wg, wg))
         sigs.append(reduce_sig(w.M - (-(-w.M // bm) - tail_rows) * bm))
     return sigs
 

@@ -144,8 +144,10 @@ int launch_rows(const GemmArgs &a, const Plan &p, int splits, unsigned grid,
     hipError_t e;
     switch (p.tile) {
     case TILE_256:
-        e = launch_tile256(a, p.loader, p.layout, out_f32, split, p.vec_out,
-                           grid, s);
+        e = p.four_wave
+                ? launch_tile256_w4(a, out_f32, split, p.vec_out, grid, s)
+                : launch_tile256(a, p.loader, p.layout, out_f32, split,
+                                 p.vec_out, grid, s);
         break;
     case TILE_128:
         e = launch_tile128(a, p.loader, p.layout, out_f32, split, p.vec_out,

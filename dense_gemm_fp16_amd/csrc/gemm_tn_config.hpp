@@ -59,6 +59,22 @@
 #ifndef GTN_T64_MFMA
 #define GTN_T64_MFMA 16
 #endif
+// Four-wave schedule of the 256 tile (TN operands, direct loads): the MFMA
+// of k-step 1 after which the tile's barrier sits, and the slots of the 16
+// tile loads in k-step 0 (after MFMA LOAD_FIRST + LOAD_EVERY * x).
+// Measured at 4096^3 (HIP events, one box, the ping-pong kernel interleaved
+// as the yardstick): loads every 4 MFMAs beat every 3, 2 or 1 (a burst of
+// 16 at the start of the k-step was 11 % slower); the barrier after MFMA
+// 32, 40 or 47 made no difference beyond noise.
+#ifndef GTN_W4_BARRIER_AT
+#define GTN_W4_BARRIER_AT 47
+#endif
+#ifndef GTN_W4_LOAD_FIRST
+#define GTN_W4_LOAD_FIRST 3
+#endif
+#ifndef GTN_W4_LOAD_EVERY
+#define GTN_W4_LOAD_EVERY 4
+#endif
 // Cache-policy bits of the staged 16-byte output stores (gfx950: 1 = sc0,
 // 2 = nt, 16 = sc1).
 #ifndef GTN_STORE_CPOL

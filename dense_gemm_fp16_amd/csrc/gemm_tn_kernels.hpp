@@ -219,6 +219,42 @@ __device__ inline void lds_fence(T (&v)[N])
         tie_reg(v[k]);
 }
 
+// v_mfma_f32_16x16x32_f16 on accumulators held in the accumulation
+// registers ("a" constraint), as asm so that the compiler can neither move
+// the accumulators to ordinary registers nor reorder the MFMAs.  acc += the
+// product of fragments b (16 columns) and a (16 rows); the _first form
+// starts the sum at +0 (as acc = 0 + product would).  The compiler does not
+// know these are MFMAs and so inserts none of their hazard padding: the
+// operands a and b must come from LDS or memory loads (whose completion the
+// compiler waits for), never from a vector-ALU write just before, and the
+// results may be read only after after_mfma16_acc.
+__device__ inline void mfma16_acc(f32x4 &acc, const half8 &b, const half8 &a)
+{
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, %0"
+                 : "+a"(acc)
+                 : "v"(b), "v"(a));
+}
+__device__ inline void mfma16_acc_first(f32x4 &acc, const half8 &b,
+                                        const half8 &a)
+{
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0"
+                 : "=a"(acc)
+                 : "v"(b), "v"(a));
+}
+// Wait states between the last asm MFMA and any read of its results (32,
+// above what an 8-pass MFMA's result needs before a vector-ALU read), then
+// every accumulator tied to the wait so that no read is scheduled before.
+template <int MI, int NI>
+__device__ inline void after_mfma16_acc(f32x4 (&acc)[MI][NI])
+{
+    asm volatile("s_nop 7\n\ts_nop 7\n\ts_nop 7\n\ts_nop 7" ::: "memory");
+#pragma unroll
+    for (int i = 0; i < MI; ++i)
+#pragma unroll
+        for (int j = 0; j < NI; ++j)
+            asm volatile("" : "+a"(acc[i][j]));
+}
+
 template <typename OutT>
 struct OutTraits;
 template <>
@@ -313,6 +349,10 @@ __device__ inline void store_out_vec4(__amdgpu_buffer_rsrc_t r, uint32_t off,
 //           registers while the other issues loads and fragment reads);
 //           2 = ping-pong with the tile loads split between the two wave
 //           groups (A ring of three stages, B ring of two);
+//           3 = four waves, one per SIMD, each multiplying a 128 x 128
+//           quadrant with its accumulators in the accumulation registers,
+//           tile loads and fragment reads at fixed slots between the MFMAs
+//           (256 x 256 x 64 tiles of TN operands only);
 //   MB : MFMA block edge, 32 (v_mfma_f32_32x32x16_f16) or 16
 //        (v_mfma_f32_16x16x32_f16: the same work per cycle, in four times as
 //        many instructions, at a lower power per flop on random data);
@@ -426,6 +466,11 @@ gemm_tn_kernel(GemmArgs p)
     // the wave's LDS base); lane l lands in physical chunk l % CHUNKS of row
     // l / CHUNKS of that group, so it fetches the logical chunk the swizzle
     // maps there.  Wave w fills row groups w, w + NW, ... of A, then of B.
+    constexpr bool FOUR_WAVE = SCHED == 3 && LOADER == LOAD_DIRECT;
+    static_assert(!FOUR_WAVE || (BM == 256 && BN == 256 && BK == 64 &&
+                                 WM == 2 && WN == 2 && STAGES == 2 &&
+                                 MB == 16 && LAY == 0),
+                  "four waves: 256 x 256 x 64 TN tiles, two stages");
     constexpr bool PINGPONG = (SCHED == 1 || SCHED == 2) &&
                               LOADER == LOAD_DIRECT;
     static_assert(!PINGPONG || (NW == 8 && STAGES == 2),
@@ -712,7 +757,173 @@ gemm_tn_kernel(GemmArgs p)
     constexpr int MFMAS = MI * NI;
 
     // ---- main loop -------------------------------------------------------
-    if constexpr (PINGPONG) {
+    if constexpr (FOUR_WAVE) {
+        // One wave per SIMD multiplies a 128 x 128 quadrant: per k-tile two
+        // k-steps of 64 MFMAs (8 x 8 blocks), with one LDS read (1 KiB a
+        // wave) or tile load slotted after given MFMAs instead of in phases:
+        //   k-step 0 of tile t: after MFMA 4f + 1 the read of fragment f of
+        //     k-step 1 (f = 0..15), after MFMA 4x + 3 tile load x of tile
+        //     t + 1 into the other stage (x = 0..15: A row groups, then B);
+        //   k-step 1 of tile t: after MFMA 47 each wave waits for its own
+        //     loads of tile t + 1 and passes the tile's one barrier (every
+        //     wave is then done with k-step 1's reads of this stage's
+        //     previous tile, and tile t + 1 is whole in LDS); after MFMAs
+        //     48..63 the reads of tile t + 1's k-step 0 fragments.
+        // Fragments are read in the order of first use (A 0, B 0..7,
+        // A 1..7), and the loads of a tile have the rest of k-step 0 and
+        // most of k-step 1 (about 1000 MFMA cycles) to land.  Past the last
+        // tile the loads start at k_end and read zeros without touching
+        // memory, so the loop has no branch; an empty K range multiplies
+        // one tile of zeros.
+        // The accumulators (8 x 8 x 4 registers) live in the accumulation
+        // registers through asm MFMAs (mfma16_acc): left to the compiler,
+        // tiles of this size copy accumulators between the two register
+        // files inside the loop.  The compiler waits for the fragment reads
+        // before the asm (plain LDS loads, whose registers it tracks); the
+        // results are read only after the padding below (after_mfma16_acc).
+        half8 fa0[MI], fb0[NI], fa1[MI], fb1[NI];
+        // Every fragment block starts on a multiple of 16 rows, where the
+        // swizzle repeats, so a read's address is one per-lane offset per
+        // k-step plus a wave-uniform part (stage, quadrant) and a constant
+        // (the block): tn_frag_offset(16 b, l, ks) = 16 b BK +
+        // tn_frag_offset(0, l, ks), checked on the host for every b, l, ks.
+        // Written so, the compiler keeps two address registers per operand
+        // instead of one per block.
+        const int frag_off[2] = {tn_frag_offset<BK, MB>(0, lane, 0),
+                                 tn_frag_offset<BK, MB>(0, lane, 1)};
+        auto rd_a = [&](int st, int ks, int i) {
+            return *(const half8 *)(lds + a_base(st) + wm * WTM * BK +
+                                    frag_off[ks] + i * MB * BK);
+        };
+        auto rd_b = [&](int st, int ks, int j) {
+            return *(const half8 *)(lds + b_base(st) + wn * WTN * BK +
+                                    frag_off[ks] + j * MB * BK);
+        };
+        // Read number f (0..15) of a k-step's fragments.
+        auto rd = [&](auto f_tag, int st, int ks, half8 (&af)[MI],
+                      half8 (&bf)[NI]) {
+            constexpr int f = decltype(f_tag)::value;
+            if constexpr (f == 0)
+                af[0] = rd_a(st, ks, 0);
+            else if constexpr (f <= NI)
+                bf[f - 1] = rd_b(st, ks, f - 1);
+            else
+                af[f - NI] = rd_a(st, ks, f - NI);
+        };
+        constexpr int BAR_AT = GTN_W4_BARRIER_AT;
+        constexpr int LOAD_FIRST = GTN_W4_LOAD_FIRST;
+        constexpr int LOAD_EVERY = GTN_W4_LOAD_EVERY;
+        static_assert(MI == 8 && NI == 8 && LOADS_PER_TILE == 16,
+                      "16 fragment reads and 16 tile loads per k-step");
+        static_assert(BAR_AT + 16 < 64, "the reads after the barrier fit");
+        static_assert(LOAD_FIRST + 15 * LOAD_EVERY < 64,
+                      "the tile loads fit in k-step 0");
+        // Tile loads.  Load x (A row groups 0..7, then B's) of wave w puts
+        // rows 32 g + 8 w .. + 7 of group g = x % 8 into LDS, lane l
+        // fetching, for physical chunk l % 8 of row 8 w + l / 8 (mod 32),
+        // the logical chunk the swizzle maps there (as issue_part does).
+        // A workgroup whose 256 rows of A and of B lie inside M and N and
+        // whose K range is whole k-tiles takes the FAST form: the lane's
+        // row and chunk in the offset register, the group's rows and the k
+        // offset in the scalar offset, no per-lane arithmetic.  Any other
+        // (edges, a K tail) puts the whole offset in the offset register,
+        // where the record count stops rows past M (N), and sends chunks at
+        // or past k_end out of range.
+        GTN_LDS _Float16 *ldsp = (GTN_LDS _Float16 *)(lds);
+        const int lrow = wave * 8 + (lane >> 3);
+        const int lkc = swizzle_chunk<BK>(lrow, lane & 7) * 8;
+        const uint32_t lane_a = (uint32_t)(lrow * lda + lkc) * 2;
+        const uint32_t lane_b = (uint32_t)(lrow * ldb + lkc) * 2;
+        const uint32_t grp_a = (uint32_t)(32 * lda) * 2;
+        const uint32_t grp_b = (uint32_t)(32 * ldb) * 2;
+        const bool rows_full = M - m0 >= BM && N - n0 >= BN;
+        auto load = [&](auto fast, int stage, int64_t k0, int x) {
+            const bool isA = x < 8;
+            const int g = x & 7;
+            GTN_LDS _Float16 *dst = ldsp +
+                                    (isA ? a_base(stage) : b_base(stage)) +
+                                    (g * 32 + wave * 8) * BK;
+            const uint32_t lane_off = isA ? lane_a : lane_b;
+            const uint32_t grp = (isA ? grp_a : grp_b) * (uint32_t)g;
+            if constexpr (decltype(fast)::value) {
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    isA ? rA : rB, (GTN_LDS void *)dst, 16, lane_off,
+                    grp + (uint32_t)k0 * 2, 0, 0);
+            } else {
+                const uint32_t off = k0 + lkc < k_end
+                                         ? lane_off + grp + (uint32_t)k0 * 2
+                                         : kOutOfRange;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    isA ? rA : rB, (GTN_LDS void *)dst, 16, off, 0, 0, 0);
+            }
+        };
+        // k-step 0 of the tile in stage `cur` (fragments in fa0 / fb0);
+        // FIRST: the tile's MFMAs start the sums; FAST: the loads of the
+        // tile at k_next take the fast form.
+        auto kstep0 = [&](auto first, auto fast, int cur, int64_t k_next) {
+            static_for<64>([&](auto t) {
+                constexpr int x = decltype(t)::value;
+                constexpr int i = x / NI, j = x % NI;
+                __builtin_amdgcn_sched_barrier(0);
+                if constexpr (decltype(first)::value)
+                    mfma16_acc_first(acc[i][j], fb0[j], fa0[i]);
+                else
+                    mfma16_acc(acc[i][j], fb0[j], fa0[i]);
+                if constexpr (x % 4 == 1)
+                    rd(Int<x / 4>{}, cur, 1, fa1, fb1);
+                if constexpr (x >= LOAD_FIRST &&
+                              (x - LOAD_FIRST) % LOAD_EVERY == 0 &&
+                              (x - LOAD_FIRST) / LOAD_EVERY < 16) {
+                    constexpr int l = (x - LOAD_FIRST) / LOAD_EVERY;
+                    load(fast, cur ^ 1, k_next, l);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        // k-step 1 of the tile in stage `cur`, then k-step 0's fragments of
+        // the next tile from stage cur ^ 1.
+        auto kstep1 = [&](int cur) {
+            static_for<64>([&](auto t) {
+                constexpr int x = decltype(t)::value;
+                constexpr int i = x / NI, j = x % NI;
+                __builtin_amdgcn_sched_barrier(0);
+                mfma16_acc(acc[i][j], fb1[j], fa1[i]);
+                if constexpr (x == BAR_AT) {
+                    wait_vmcnt<0>();
+                    block_sync();
+                }
+                if constexpr (x > BAR_AT && x - BAR_AT <= 16)
+                    rd(Int<x - BAR_AT - 1>{}, cur ^ 1, 0, fa0, fb0);
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        };
+        const int nt = ktiles > 0 ? ktiles : 1;
+        // The whole pipeline in one load form.  Past the last tile the fast
+        // form loads the last tile again (into the stage nobody reads
+        // again, within the operands), the other form reads zeros without
+        // touching memory; either way the loop has no branch inside.
+        auto pipeline = [&](auto fast) {
+            constexpr bool F = decltype(fast)::value;
+            auto k_of = [&](int t) {
+                return k_begin + (int64_t)(F && t >= nt ? nt - 1 : t) * BK;
+            };
+            static_for<16>([&](auto x) { load(fast, 0, k_begin, x); });
+            wait_vmcnt<0>();
+            block_sync();
+            static_for<16>([&](auto f) { rd(f, 0, 0, fa0, fb0); });
+            kstep0(Bool<true>{}, fast, 0, k_of(1));
+            for (int kt = 1; kt < nt; ++kt) {
+                kstep1((kt - 1) & 1);
+                kstep0(Bool<false>{}, fast, kt & 1, k_of(kt + 1));
+            }
+            kstep1((nt - 1) & 1);
+        };
+        if (rows_full && ktiles > 0 && (k_end - k_begin) % BK == 0)
+            pipeline(Bool<true>{});
+        else
+            pipeline(Bool<false>{});
+        after_mfma16_acc(acc);
+    } else if constexpr (PINGPONG) {
         // Waves 0..3 (group 0) and 4..7 (group 1) share the SIMDs pairwise.
         // Each wave alternates a load phase (group 0 also issues the global
         // loads of the next tile; then fragments of the whole current tile

@@ -14,6 +14,10 @@ namespace gtn {
 hipError_t launch_tile256(const GemmArgs &a, int loader, int layout,
                           bool out_f32, bool split, bool vec_out,
                           unsigned grid, hipStream_t s);
+// The 256 tile of TN operands with direct loads and 16-byte output rows,
+// on four waves.
+hipError_t launch_tile256_w4(const GemmArgs &a, bool out_f32, bool split,
+                             bool vec_out, unsigned grid, hipStream_t s);
 hipError_t launch_tile128(const GemmArgs &a, int loader, int layout,
                           bool out_f32, bool split, bool vec_out,
                           unsigned grid, hipStream_t s);

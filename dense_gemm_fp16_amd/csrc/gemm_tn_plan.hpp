@@ -82,6 +82,10 @@ struct Plan {
     // Persistent one-k-tile kernel (K <= kOneK, 128 x 128 tiles, `grid`
     // workgroups walking tiles_m * tiles_n * batch tiles).
     bool onek = false;
+    // The 256 tile of TN operands with direct loads and 16-byte output rows
+    // runs on four waves, one per SIMD (2 x 2 quadrants of 128 x 128),
+    // instead of eight.
+    bool four_wave = false;
 };
 
 constexpr int64_t kOneK = 64;           // deepest K the one-k-tile kernel takes
@@ -177,13 +181,14 @@ inline int check_pointers(int64_t M, int64_t N, int64_t K, const void *A,
 }
 
 // Optional override for tuning sweeps and tests: "tile=256|128|64,
-// loader=0|1|2,split=S,group=G,tail=R,tail_split=T,onek=0|1" (any subset,
-// comma separated; tail=0 turns the tail split off; onek=1 takes the
-// persistent one-k-tile kernel wherever it applies, onek=0 never).  Unknown keys are ignored;
-// a loader that the operands' alignment does not allow is ignored.
+// loader=0|1|2,split=S,group=G,tail=R,tail_split=T,onek=0|1,w4=0|1" (any
+// subset, comma separated; tail=0 turns the tail split off; onek=1 takes
+// the persistent one-k-tile kernel wherever it applies, onek=0 never; w4=0
+// runs the 256 tile of TN operands on eight waves).  Unknown keys are
+// ignored; a loader that the operands' alignment does not allow is ignored.
 struct Override {
     int tile = -1, loader = -1, split = -1, group = -1, tail = -1,
-        tail_split = -1, onek = -1;
+        tail_split = -1, onek = -1, w4 = -1;
 };
 
 inline Override parse_override(const char *s)
@@ -217,6 +222,8 @@ inline Override parse_override(const char *s)
             o.tail_split = v >= 2 ? v : -1;
         else if (!strcmp(tok, "onek"))
             o.onek = v == 0 || v == 1 ? v : -1;
+        else if (!strcmp(tok, "w4"))
+            o.w4 = v == 0 || v == 1 ? v : -1;
     }
     return o;
 }
@@ -332,6 +339,8 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         p.k_split = cdiv(K, kBK) * kBK;
 
     p.loader = loader;
+    p.four_wave = tile == TILE_256 && loader == PLAN_LOAD_DIRECT &&
+                  layout == 0 && vec_out && o.w4 != 0;
     p.a_mn = ld.a_mn;
     p.b_mn = ld.b_mn;
     p.layout = layout;
@@ -451,10 +460,12 @@ inline int describe_plan(const Plan &p, char *buf, int64_t buflen)
              p.bm, p.bn,
              p.splits > 1 ? kTileSplitBK[p.tile] : kTileBK[p.tile],
              p.splits > 1 ? kTileSplitStages[p.tile] : kTileStages[p.tile],
-             kTileWM[p.tile], kTileWN[p.tile], kTileMfma[p.tile],
+             p.four_wave ? 2 : kTileWM[p.tile],
+             p.four_wave ? 2 : kTileWN[p.tile], kTileMfma[p.tile],
              kTileMfma[p.tile],
-             p.loader == PLAN_LOAD_DIRECT ? scheds[kTileSched[p.tile]]
-                                          : "staged",
+             p.four_wave                    ? "four-wave"
+             : p.loader == PLAN_LOAD_DIRECT ? scheds[kTileSched[p.tile]]
+                                            : "staged",
              loaders[p.loader], p.a_mn ? "m" : "k", p.b_mn ? "n" : "k",
              p.splits,
              (long long)p.k_split, p.vec_out ? 1 : 0, p.group_m,

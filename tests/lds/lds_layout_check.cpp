@@ -119,6 +119,19 @@ static void gemm_tile()
                 check_access(addr, 16, "B fragment read", BN, w, ks, j);
             }
         }
+    // Every MB-row block starts where the swizzle repeats (16 rows), so a
+    // block's fragment offsets are the first block's shifted by whole rows
+    // (the four-wave kernel reads with one per-lane offset per k-step).
+    if (MB == 16)
+        for (int ks = 0; ks < KSTEPS; ++ks)
+            for (int b = 0; b < (BM > BN ? BM : BN) / MB; ++b)
+                for (int l = 0; l < 64; ++l) {
+                    ++g_checks;
+                    if (tn_frag_offset<BK, MB>(b * MB, l, ks) !=
+                        b * MB * BK + tn_frag_offset<BK, MB>(0, l, ks))
+                        fail("fragment offset not block-invariant", b, l, ks,
+                             BK);
+                }
     // Register-staged loaders: thread t writes chunk slot t of each block of
     // NT / CHUNKS rows (A rows first), 16 bytes to its swizzled chunk.
     constexpr int RB = NT / CHUNKS;
@@ -323,6 +336,7 @@ int main()
     // GEMM tiles as instantiated (16 x 16 MFMA blocks) and the 32 x 32
     // alternative the tiles can be built with.
     gemm_tile<256, 256, 64, 2, 4, 16>();
+    gemm_tile<256, 256, 64, 2, 2, 16>();      // four waves, 128 x 128 each
     gemm_tile<128, 128, 64, 2, 2, 16>();
     gemm_tile<64, 64, 64, 2, 2, 16>();
     gemm_tile<256, 256, 64, 2, 4, 32>();
@@ -341,10 +355,13 @@ int main()
         mn_tile<64, 64>(w * 32, 2);
         mn_tile<64, 128>(w * 32, 2);          // 128 k-rows
     }
-    // Epilogue staging: wave sub-tiles of the 256 and 128 tiles (128 x 64,
-    // 64 x 64) and the 64 tile (32 x 32), fp16, fp32 and split-K partials.
+    // Epilogue staging: wave sub-tiles of the 256 tile on eight and on four
+    // waves (128 x 64, 128 x 128), the 128 tile (64 x 64) and the 64 tile
+    // (32 x 32), fp16, fp32 and split-K partials.
     epilogue<128, 64, 2, 16>();
     epilogue<128, 64, 4, 16>();
+    epilogue<128, 128, 2, 16>();
+    epilogue<128, 128, 4, 16>();
     epilogue<64, 64, 2, 16>();
     epilogue<64, 64, 4, 16>();
     epilogue<32, 32, 2, 16>();

@@ -188,10 +188,12 @@ def describe(batch, M, N, K, beta=0.0, out="f16", aligned=True, lds=None,
 
 
 def test_plans_for_the_workloads():
-    # 4096^3: one 256x256 tile per CU, vector loader, no split
+    # 4096^3: one 256x256 tile per CU, vector loader, no split, on four
+    # waves (one per SIMD)
     p = describe(1, 4096, 4096, 4096)
     assert p["tile"].startswith("256x256x") and p["split"] == "1"
     assert p["grid"] == "256" and p["loader"] != "elem"
+    assert (p["waves"], p["sched"]) == ("2x2", "four-wave")
     # 1024^3 and the ragged 1000x1030x1000: 64x64 tiles, enough of them
     # (whole-K problems on the 64 tile take its two-stage ring of 128-deep
     # k-tiles)
@@ -253,6 +255,26 @@ def test_tail_split_plans(monkeypatch):
     assert (p["tail_rows"], p["tail_split"]) == ("2", "3")
     assert p["grid"] == str((10 - 2) * 5 * 2)
     assert p["tail_grid"] == str(2 * 5 * 2 * 3)
+
+
+def test_four_wave_plans(monkeypatch):
+    # four waves need TN operands, direct loads and 16-byte output rows;
+    # otherwise (and with w4=0) the 256 tile runs on eight
+    assert describe(1, 4096, 4096, 4096, 0.5, "f32")["sched"] == "four-wave"
+    p = describe(1, 4096, 4100, 4096)        # 8200-byte rows: no 16-byte
+    assert p["tile"].startswith("256x256x") and p["vec_out"] == "0"
+    assert (p["waves"], p["sched"]) == ("2x4", "pingpong-split")
+    p = describe(1, 4096, 4096, 4096, layouts=(1, 0))
+    assert (p["waves"], p["sched"]) == ("2x4", "pingpong-split")
+    monkeypatch.setenv("GEMM_TN_FORCE", "w4=0")
+    p = describe(1, 4096, 4096, 4096)
+    assert (p["waves"], p["sched"]) == ("2x4", "pingpong-split")
+    # split-K slices and the tail split keep four waves
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256,split=3")
+    assert describe(1, 512, 512, 4096)["sched"] == "four-wave"
+    monkeypatch.delenv("GEMM_TN_FORCE")
+    p = describe(1, 4352, 4352, 4096)
+    assert p["tail_rows"] != "0" and p["sched"] == "four-wave"
 
 
 def test_override_spec(monkeypatch):

@@ -138,7 +138,10 @@ def test_edge_shapes_bit_exact(out):
 
 
 CONFIGS = [f"tile={t},loader={l},split={s}" for t in (256, 128, 64)
-           for l in (0, 1, 2) for s in (1, 3)]
+           for l in (0, 1, 2) for s in (1, 3)] + [
+    # the 256 tile of TN operands on eight waves (four is the default where
+    # the output rows allow 16-byte stores)
+    "tile=256,loader=0,split=1,w4=0", "tile=256,loader=0,split=3,w4=0"]
 
 
 @pytest.mark.parametrize("spec", CONFIGS)
@@ -146,6 +149,7 @@ def test_every_kernel_configuration(spec, monkeypatch):
     """Each tile x loader x split-K instantiation on ragged shapes."""
     monkeypatch.setenv("GEMM_TN_FORCE", spec)
     for (batch, M, N, K, out, beta) in [(1, 300, 260, 832, "f16", 0.0),
+                                        (1, 300, 264, 832, "f16", 0.5),
                                         (2, 129, 200, 1000, "f32", -2.0),
                                         (1, 512, 516, 768, "f32", 0.5)]:
         w = _int_workload(batch, M, N, K, out, alpha=0.5, beta=beta)
@@ -154,6 +158,45 @@ def test_every_kernel_configuration(spec, monkeypatch):
         ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
         res = oracle.check_exact(d, ref, out)
         assert res.ok, f"{spec} {M}x{N}x{K}: {res}"
+
+
+FOUR_WAVE_SHAPES = [
+    # (batch, M, N, K, out, alpha, beta)
+    (1, 300, 264, 832, "f16", 1.0, 0.0),     # ragged M and N, alpha = 1
+    (1, 257, 520, 1000, "f16", -1.5, 0.5),   # K tail (1000 = 15 x 64 + 40)
+    (2, 129, 136, 72, "f32", 0.5, -2.0),     # two k-tiles, the second of 8
+    (1, 256, 256, 64, "f16", 1.0, 0.0),      # exactly one k-tile
+    (1, 256, 256, 8, "f32", 2.0, 0.0),       # K below one k-tile
+    (3, 512, 256, 200, "f32", 1.0, 1.0),     # batches, several tiles
+]
+
+
+@pytest.mark.parametrize("shape", FOUR_WAVE_SHAPES)
+def test_four_wave_kernel_bit_exact(shape, monkeypatch):
+    """The 256 tile's four-wave kernel on ragged shapes: M and N tails,
+    K tails and a single k-tile, batches, with and without C."""
+    batch, M, N, K, out, alpha, beta = shape
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256")
+    desc = _gpu().describe(batch, M, N, K, beta, out)
+    assert "sched=four-wave" in desc, desc
+    w = _int_workload(batch, M, N, K, out, alpha=alpha, beta=beta)
+    _say(f"[four-wave] {batch}x{M}x{N}x{K} {out} alpha={alpha} beta={beta}")
+    d = run_gpu(w)
+    ref = oracle.gemm_tn(w.A, w.B, w.alpha, w.beta, w.C)
+    res = oracle.check_exact(d, ref, out)
+    assert res.ok, f"{shape}: {res}"
+
+
+def test_four_wave_kernel_with_k_zero(monkeypatch):
+    """An empty K range multiplies one tile of zeros: D = beta * C."""
+    g = _gpu()
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256")
+    assert "sched=four-wave" in g.describe(1, 300, 260, 0, 0.5, "f32")
+    A = torch.empty(300, 0, dtype=torch.float16, device="cuda")
+    B = torch.empty(260, 0, dtype=torch.float16, device="cuda")
+    C = torch.randn(300, 260, device="cuda")
+    D = g.gemm_tn(A, B, 2.0, -0.5, C)
+    assert torch.equal(D, -0.5 * C)
 
 
 def test_unaligned_operands_and_odd_k():

@@ -1171,7 +1171,9 @@ gemm_tn_kernel(GemmArgs p)
     char *region = (char *)lds + wave * REGION;
 
     // Fp32 results of the block in output precision, then into the slice.
-    auto stage_pass = [&](int pass, auto finish) {
+    // BARE: finish returns the accumulators themselves, which no product
+    // precedes, so the conversion needs no barrier (to_half).
+    auto stage_pass = [&](int pass, auto finish, auto bare) {
 #pragma unroll
         for (int ii = 0; ii < RPP / MB; ++ii) {
             const int i = pass * (RPP / MB) + ii;
@@ -1186,8 +1188,10 @@ gemm_tn_kernel(GemmArgs p)
                     const int col = j * MB + 4 * QN * g + en;  // element column
                     const int cb = col * ES;                  // byte column
                     char *dst = region + stage_offset<ROW_BYTES>(r, cb);
-                    if (ES == 4) {
+                    if constexpr (ES == 4) {
                         *(f32x4 *)dst = v;
+                    } else if constexpr (decltype(bare)::value) {
+                        *(half4 *)dst = __builtin_convertvector(v, half4);
                     } else {
                         half4 h = to_half4(v);
                         *(half4 *)dst = h;
@@ -1196,20 +1200,34 @@ gemm_tn_kernel(GemmArgs p)
         }
     };
     // Slice rows back out, 16 bytes per lane, row-contiguous.
+    // A lane keeps its 16-byte column c = lane % CPR in every iteration
+    // (CPR divides 64), and its row advances by 64 / CPR: one column check
+    // and one 32-bit offset per pass, then an add per store (offsets are
+    // below 2^31: the resource starts at the tile's first row, and rows
+    // and columns are limited to 2^20 elements).  A column past n_limit
+    // starts at kOutOfRange, which the adds keep out of range.
+    // The LDS reads take stage_read_period addresses and constant offsets.
+    static_assert(64 % CPR == 0, "a lane's column is fixed across stores");
+    constexpr int RPER = stage_read_period<ROW_BYTES>();
     auto drain_pass = [&](int pass, __amdgpu_buffer_rsrc_t rOut, int64_t ld,
                           int64_t n_limit) {
+        const int c = lane % CPR;
+        const int64_t n = n0 + wn * WTN + c * (16 / ES);
+        const int lm0 = wm * WTM + pass * RPP + lane / CPR;
+        const uint32_t base =
+            n < n_limit ? (uint32_t)((lm0 * ld + n) * ES) : kOutOfRange;
+        const uint32_t step = (uint32_t)(64 / CPR * ld * ES);
+        int roff[RPER];
+#pragma unroll
+        for (int q = 0; q < RPER; ++q)
+            roff[q] = stage_read_offset<ROW_BYTES>(lane, q);
 #pragma unroll
         for (int it = 0; it < RPP * CPR / 64; ++it) {
-            const int idx = it * 64 + lane;
-            const int r = idx / CPR, c = idx % CPR;
-            const u32x4 v =
-                *(const u32x4 *)(region + stage_offset<ROW_BYTES>(r, c * 16));
-            const int lm = wm * WTM + pass * RPP + r;
-            const int64_t n = n0 + wn * WTN + c * (16 / ES);
-            const uint32_t off =
-                n < n_limit ? (uint32_t)((lm * ld + n) * ES) : kOutOfRange;
-            __builtin_amdgcn_raw_buffer_store_b128(v, rOut, off, 0,
-                                                   GTN_STORE_CPOL);
+            const u32x4 v = *(const u32x4 *)(
+                region + roff[it % RPER] +
+                (it / RPER) * (RPER * (64 / CPR) * ROW_BYTES));
+            __builtin_amdgcn_raw_buffer_store_b128(
+                v, rOut, base + (uint32_t)it * step, 0, GTN_STORE_CPOL);
         }
     };
 
@@ -1228,7 +1246,8 @@ gemm_tn_kernel(GemmArgs p)
             make_rsrc(wsb, (M - m0) * p.ws_ld * 4);
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
-            stage_pass(pass, [](int, int, int, f32x4 v) { return v; });
+            stage_pass(pass, [](int, int, int, f32x4 v) { return v; },
+                       Bool<true>{});
             drain_pass(pass, rW, p.ws_ld, N);
         }
         return;
@@ -1268,11 +1287,11 @@ gemm_tn_kernel(GemmArgs p)
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
             if (use_c)
-                stage_pass(pass, with_c);
+                stage_pass(pass, with_c, Bool<false>{});
             else if (alpha == 1.0f)
-                stage_pass(pass, as_is);
+                stage_pass(pass, as_is, Bool<true>{});
             else
-                stage_pass(pass, no_c);
+                stage_pass(pass, no_c, Bool<false>{});
             drain_pass(pass, rD, ldd, N);
         }
         return;
@@ -1287,7 +1306,8 @@ gemm_tn_kernel(GemmArgs p)
         static_assert(RPP * EPR % 64 == 0, "whole waves of elements");
 #pragma unroll
         for (int pass = 0; pass < PASSES; ++pass) {
-            stage_pass(pass, [&](int, int, int, f32x4 v) { return v * alpha; });
+            stage_pass(pass, [&](int, int, int, f32x4 v) { return v * alpha; },
+                       Bool<false>{});
 #pragma unroll
             for (int it = 0; it < RPP * EPR / 64; ++it) {
                 const int idx = it * 64 + lane;

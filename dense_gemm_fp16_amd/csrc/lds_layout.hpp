@@ -117,6 +117,36 @@ __device__ __host__ constexpr int stage_offset(int r, int cb)
     return r * ROW_BYTES + stage_chunk<ROW_BYTES>(r, cb / 16) * 16 + cb % 16;
 }
 
+// Row reads of the staging: read `it` of a wave takes 16 bytes at row
+// it * RS + lane / CPR, chunk lane % CPR (RS = 64 / CPR rows per read).
+template <int ROW_BYTES>
+__device__ __host__ constexpr int stage_read_offset(int lane, int it)
+{
+    constexpr int CPR = ROW_BYTES / 16;
+    return stage_offset<ROW_BYTES>(it * (64 / CPR) + lane / CPR,
+                                   (lane % CPR) * 16);
+}
+// The swizzle term of those rows repeats every stage_read_period reads, so
+// stage_read_offset(l, it) = stage_read_offset(l, it % P) +
+// (it / P) * P * RS * ROW_BYTES: P address registers and constant offsets
+// (checked on the host for every lane and read).
+template <int ROW_BYTES>
+__device__ __host__ constexpr int stage_read_period()
+{
+    constexpr int CPR = ROW_BYTES / 16;
+    constexpr int RS = 64 / CPR;
+    constexpr int LINE_ROWS = ROW_BYTES >= 256 ? 1 : 256 / ROW_BYTES;
+    constexpr int X = CPR < 16 ? CPR : 16;
+    static_assert(RS % LINE_ROWS == 0, "reads cover whole 256-byte lines");
+    int a = X, b = RS / LINE_ROWS;          // P = X / gcd(X, RS / LINE_ROWS)
+    while (b != 0) {
+        const int t = a % b;
+        a = b;
+        b = t;
+    }
+    return X / a;
+}
+
 // V tile of the attention kernel (64-element = 128-byte rows of keys), read
 // with ds_read_b64_tr_b16: a half wave reads 8 consecutive key rows at one
 // pair of 16-byte chunks (c, c + 1), c even.  Rows of one parity share a

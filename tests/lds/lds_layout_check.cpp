@@ -205,7 +205,17 @@ static void epilogue()
                 check_access(addr, 4 * ES, "epilogue staging write", WTN, ES,
                              ii, j);
             }
-    // 16-byte row reads
+    // 16-byte row reads, and their split into a periodic per-lane part and
+    // a constant
+    constexpr int P = stage_read_period<ROW_BYTES>();
+    for (int it = 0; it < WTM * CPR / 64; ++it)
+        for (int l = 0; l < 64; ++l) {
+            ++g_checks;
+            if (stage_read_offset<ROW_BYTES>(l, it) !=
+                stage_read_offset<ROW_BYTES>(l, it % P) +
+                    (it / P) * P * (64 / CPR) * ROW_BYTES)
+                fail("staged row read offset not periodic", WTN, ES, it, l);
+        }
     for (int it = 0; it < WTM * CPR / 64; ++it) {
         for (int l = 0; l < 64; ++l) {
             const int idx = it * 64 + l;

@@ -136,6 +136,12 @@ __global__ void __launch_bounds__(256) gemm_onek_kernel(GemmArgs p)
     };
 
     char *region = lds + NBUF * OP * 2 + wave * REGION;
+    static_assert(64 % CPR == 0, "a lane's column is fixed across stores");
+    constexpr int RPER = stage_read_period<ROW_BYTES>();
+    int roff[RPER];
+#pragma unroll
+    for (int q = 0; q < RPER; ++q)
+        roff[q] = stage_read_offset<ROW_BYTES>(lane, q);
     if (count > 0) {
 #pragma unroll
         for (int i = 0; i < DEPTH; ++i)
@@ -220,17 +226,26 @@ __global__ void __launch_bounds__(256) gemm_onek_kernel(GemmArgs p)
                     *(half4 *)dst = h;
                 }
             }
-#pragma unroll
-        for (int it = 0; it < STORES; ++it) {
-            const int idx = it * 64 + lane;
-            const int rr = idx / CPR, c = idx % CPR;
-            const u32x4 v =
-                *(const u32x4 *)(region + stage_offset<ROW_BYTES>(rr, c * 16));
+        // A lane keeps its 16-byte column in every store (CPR divides 64)
+        // and its row advances by 64 / CPR: one column check and one 32-bit
+        // offset per tile (below 2^31: the resource starts at the tile's
+        // first row), an add per store; the staged rows are read at
+        // stage_read_period addresses plus constants.
+        {
+            const int c = lane % CPR;
             const int64_t n = t.n0 + wn * WT + c * (16 / ES);
-            const int m = wm * WT + rr;
-            __builtin_amdgcn_raw_buffer_store_b128(
-                v, rD, n < N ? (uint32_t)((m * ldd + n) * ES) : kOutOfRange,
-                0, GTN_ONEK_CPOL);
+            const int m = wm * WT + lane / CPR;
+            const uint32_t base =
+                n < N ? (uint32_t)((m * ldd + n) * ES) : kOutOfRange;
+            const uint32_t step = (uint32_t)(64 / CPR * ldd * ES);
+#pragma unroll
+            for (int it = 0; it < STORES; ++it) {
+                const u32x4 v = *(const u32x4 *)(
+                    region + roff[it % RPER] +
+                    (it / RPER) * (RPER * (64 / CPR) * ROW_BYTES));
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, rD, base + (uint32_t)it * step, 0, GTN_ONEK_CPOL);
+            }
         }
     }
     wait_vmcnt<0>();

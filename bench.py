@@ -29,6 +29,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import re
 import os
 import platform
 import sys
@@ -392,6 +393,16 @@ def trace_signatures(w):
     return sigs
 
 
+def _name_has(part, name):
+    """Whether a kernel name from a trace holds `part`, which names a tile
+    kernel in its mangled form (gemm_tn_kernelILi256ELi256E): rocprofv3
+    reports some names demangled (gemm_tn_kernel<256, 256, ...>)."""
+    if part in name:
+        return True
+    m = re.fullmatch(r"(\w+?)ILi(\d+)ELi(\d+)E", part)
+    return bool(m) and f"{m.group(1)}<{m.group(2)}, {m.group(3)}, " in name
+
+
 def summarize_trace_all(csv_path, bench_jsonl=None):
     """Markdown table of the kernel times of every configuration in one
     rocprofv3 kernel trace (a --all run): each kernel of a call is found by
@@ -421,7 +432,7 @@ def summarize_trace_all(csv_path, bench_jsonl=None):
         for part, grid, wg in trace_signatures(w):
             d = [int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
                  for r in rows
-                 if part in r["Kernel_Name"]
+                 if _name_has(part, r["Kernel_Name"])
                  and int(r["Grid_Size_X"]) == grid
                  and int(r["Workgroup_Size_X"]) == wg]
             if not d:

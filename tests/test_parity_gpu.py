@@ -637,6 +637,25 @@ def test_largest_k(spec, monkeypatch):
     assert res.ok, str(res)
 
 
+@pytest.mark.parametrize("K", [2 ** 16, 2 ** 16 + 40])
+def test_four_wave_kernel_long_k(K, monkeypatch):
+    """The four-wave 256 tile over 1024 k-tiles: whole tiles take the loads
+    with the k offset in the scalar offset (K = 2^16), a K tail the per-lane
+    form; values in {-1, 0, 1} keep every sum exact."""
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256")
+    M = N = 256
+    desc = _gpu().describe(1, M, N, K, 0.0, "f32")
+    assert "sched=four-wave" in desc, desc
+    w = si.build("longk", 1, M, N, K, 1.0, 0.0, "f32", "int", 0x5EED0A02)
+    w.A = (w.A.astype(np.float32) // 2).clip(-1, 1).astype(np.float16)
+    w.B = (w.B.astype(np.float32) // 2).clip(-1, 1).astype(np.float16)
+    _say(f"[four-wave] K={K}: {desc}")
+    d = run_gpu(w)
+    ref = oracle.gemm_tn(w.A, w.B)
+    res = oracle.check_exact(d, ref, "f32")
+    assert res.ok, str(res)
+
+
 def test_largest_n_and_a_long_m():
     """N = 2^20, the largest supported, and M past a million rows
     (sampled), on integer values."""

@@ -765,16 +765,17 @@ gemm_tn_kernel(GemmArgs p)
         //     k-step 1 (f = 0..15), after MFMA 4x + 3 tile load x of tile
         //     t + 1 into the other stage (x = 0..15: A row groups, then B);
         //   k-step 1 of tile t: after MFMA 47 each wave waits for its own
-        //     loads of tile t + 1 and passes the tile's one barrier (every
-        //     wave is then done with k-step 1's reads of this stage's
-        //     previous tile, and tile t + 1 is whole in LDS); after MFMAs
-        //     48..63 the reads of tile t + 1's k-step 0 fragments.
+        //     loads of tile t + 1 and for its LDS reads, and passes the
+        //     tile's one barrier: tile t + 1 is then whole in LDS, and every
+        //     read of tile t's stage, which the loads of tile t + 2 refill
+        //     next, is done; after MFMAs 48..63 the reads of tile t + 1's
+        //     k-step 0 fragments.
         // Fragments are read in the order of first use (A 0, B 0..7,
         // A 1..7), and the loads of a tile have the rest of k-step 0 and
         // most of k-step 1 (about 1000 MFMA cycles) to land.  Past the last
-        // tile the loads start at k_end and read zeros without touching
-        // memory, so the loop has no branch; an empty K range multiplies
-        // one tile of zeros.
+        // tile the loads read zeros without touching memory (or, in the
+        // fast form below, the last tile again), so the loop has no branch;
+        // an empty K range multiplies one tile of zeros.
         // The accumulators (8 x 8 x 4 registers) live in the accumulation
         // registers through asm MFMAs (mfma16_acc): left to the compiler,
         // tiles of this size copy accumulators between the two register
@@ -890,6 +891,7 @@ gemm_tn_kernel(GemmArgs p)
                 mfma16_acc(acc[i][j], fb1[j], fa1[i]);
                 if constexpr (x == BAR_AT) {
                     wait_vmcnt<0>();
+                    wait_lgkmcnt<0>();
                     block_sync();
                 }
                 if constexpr (x > BAR_AT && x - BAR_AT <= 16)

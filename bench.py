@@ -523,7 +523,8 @@ def roofline_of(w, sec, traffic=None):
     return tflops, gbs, roof
 
 
-# The configurations of the study, in the order of the survey's table.
+# The configurations of the study: the small square product, 1024^3 with
+# C, the 4096^3 headline, the two ragged shapes and the batched score product.
 CONFIGS = ("c1_256", "c2_1024", "c3_4096", "c4a_ragged", "c4b_skinny",
            "c5_qk")
 

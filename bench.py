@@ -205,6 +205,12 @@ def _args():
                     help="also time torch.matmul (the vendor BLAS) on the "
                          "same inputs, interleaved with this library "
                          "(context only; plain products)")
+    ap.add_argument("--plan-grid", nargs="?", const=PLAN_GRID_SHAPES,
+                    metavar="BxMxNxK,...",
+                    help="time every tile x split-K choice and the "
+                         "planner's own on each shape (JSON lines)")
+    ap.add_argument("--summarize-plan-grid", metavar="PLAN_GRID_JSONL",
+                    help="markdown table of a --plan-grid run")
     ap.add_argument("--summarize-trace", metavar="KERNEL_TRACE_CSV",
                     help="median / min / max kernel time per call of "
                          "--workload from a rocprofv3 kernel_trace.csv")
@@ -309,6 +315,115 @@ def time_vendor_interleaved(w, rounds=6, burst=10):
             torch.cuda.synchronize()
             times[name].append(start.elapsed_time(stop) / 1e3 / burst)
     return {k: statistics.median(v) for k, v in times.items()}
+
+
+PLAN_GRID_SPLITS = (1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32, 48, 64)
+PLAN_GRID_SHAPES = (
+    "1x512x512x2048,1x512x512x8192,1x768x768x4096,1x1024x1024x2048,"
+    "1x1024x1024x4096,1x1024x1024x8192,1x1024x1024x16384,1x1536x1536x2048,"
+    "1x1536x1536x4096,1x1536x1536x8192,1x2048x2048x2048,1x2048x2048x4096,"
+    "1x2048x2048x8192,1x2560x2560x4096,1x3072x3072x2048,1x3072x3072x4096,"
+    "1x256x256x16384,1x256x2048x8192,1x512x4096x4096,1x2816x2816x6144,"
+    "2x1024x1024x4096")
+
+
+def plan_grid(shapes, rounds=4, burst=10):
+    """For each BxMxNxK shape (fp16 D, alpha 1, beta 0): the median time per
+    call of every tile x split-K choice (forced, slices of at least 256
+    along K, partials within the no-allocation scratch) and of the
+    planner's own choice, in interleaved bursts of `burst` calls, HIP
+    events around each burst.  One JSON line per shape."""
+    import statistics
+    import torch
+    import dense_gemm_fp16_amd as g
+
+    def cdiv(x, y):
+        return -(-x // y)
+
+    def plan_of(b, M, N, K):
+        d = dict(kv.split("=") for kv in g.describe(b, M, N, K).split())
+        return int(d["tile"].split("x")[0]), int(d["split"])
+
+    gen = torch.Generator(device="cuda")
+    for tok in shapes.split(","):
+        b, M, N, K = (int(x) for x in tok.split("x"))
+        specs = {}
+        for tile in (256, 128, 64):
+            if tile == 256 and (M < 256 or N < 256):
+                continue
+            for s in PLAN_GRID_SPLITS:
+                if s > 1 and K // s < 256:
+                    break
+                se = cdiv(K, cdiv(cdiv(K, s), 64) * 64)
+                if se > 1 and se * b * M * cdiv(N, 4) * 16 > \
+                        g.NOALLOC_SCRATCH_BYTES:
+                    break
+                specs.setdefault((tile, se), f"tile={tile},split={se},tail=0")
+        gen.manual_seed(b * 7919 + M * 31 + N * 17 + K)
+        A = (torch.rand(b, M, K, device="cuda", generator=gen) * 2 - 1).half()
+        B = (torch.rand(b, N, K, device="cuda", generator=gen) * 2 - 1).half()
+        D = torch.empty(b, M, N, device="cuda", dtype=torch.float16)
+        runs = [("planner", "")] + [(k, v) for k, v in specs.items()]
+        times = {k: [] for k, _ in runs}
+        start = torch.cuda.Event(enable_timing=True)
+        stop = torch.cuda.Event(enable_timing=True)
+        old = os.environ.get("GEMM_TN_FORCE")
+        try:
+            for _ in range(rounds):
+                for key, spec in runs:
+                    os.environ["GEMM_TN_FORCE"] = spec
+                    g.gemm_tn(A, B, out=D)
+                    g.gemm_tn(A, B, out=D)
+                    start.record()
+                    for _ in range(burst):
+                        g.gemm_tn(A, B, out=D)
+                    stop.record()
+                    stop.synchronize()
+                    times[key].append(start.elapsed_time(stop) * 1e3 / burst)
+            for key, spec in runs[1:]:
+                os.environ["GEMM_TN_FORCE"] = spec
+                assert plan_of(b, M, N, K) == key, (tok, key)
+            os.environ["GEMM_TN_FORCE"] = ""
+            chosen = plan_of(b, M, N, K)
+        finally:
+            if old is None:
+                os.environ.pop("GEMM_TN_FORCE", None)
+            else:
+                os.environ["GEMM_TN_FORCE"] = old
+        med = {k: statistics.median(v) for k, v in times.items()}
+        print(json.dumps({
+            "shape": [b, M, N, K], "rounds": rounds, "burst": burst,
+            "planner": {"tile": chosen[0], "split": chosen[1],
+                        "us": round(med["planner"], 2)},
+            "choices": [[k[0], k[1], round(med[k], 2)] for k in specs]}),
+            flush=True)
+        del A, B, D
+
+
+def summarize_plan_grid(path):
+    """Markdown table of a --plan-grid run: per shape the planner's choice
+    and the fastest choice, each with its time, and their ratio."""
+    rows, ratios = [], []
+    for line in open(path):
+        if not line.startswith("{"):
+            continue
+        r = json.loads(line)
+        best = min(r["choices"], key=lambda c: c[2])
+        p = r["planner"]
+        own = [c for c in r["choices"] if c[0] == p["tile"] and
+               c[1] == p["split"]]
+        t = own[0][2] if own else p["us"]
+        ratios.append(t / best[2])
+        b, M, N, K = r["shape"]
+        rows.append(f"| {b}x{M}x{N}x{K} | {p['tile']} / {p['split']} | "
+                    f"{t:.2f} | {best[0]} / {best[1]} | {best[2]:.2f} | "
+                    f"{t / best[2]:.3f} |")
+    out = ["| batch x M x N x K | planner: tile / split | us | fastest: "
+           "tile / split | us | ratio |", "|---|---|---|---|---|---|"]
+    out += rows
+    out.append(f"\nplanner / fastest: mean {sum(ratios) / len(ratios):.3f}, "
+               f"max {max(ratios):.3f} over {len(ratios)} shapes")
+    return "\n".join(out)
 
 
 def time_workload_cold(w, steps):
@@ -920,6 +1035,9 @@ def main():
     if a.summarize_trace_all:
         print(summarize_trace_all(*a.summarize_trace_all[:2]))
         return
+    if a.summarize_plan_grid:
+        print(summarize_plan_grid(a.summarize_plan_grid))
+        return
     if a.summarize_pmc:
         t = summarize_pmc(a.summarize_pmc[0], a.summarize_pmc[1], a.workload,
                           a.calibration_mib)
@@ -945,6 +1063,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.plan_grid:
+        plan_grid(a.plan_grid)
+        return
     if a.workload in TRANSPOSES:
         transpose_main(a)
         return

@@ -29,7 +29,7 @@ GEMM_TN_ROW_K, GEMM_TN_ROW_MN = 0, 1
  ERR_SCRATCH) = range(6)
 # fixed per-GPU split-K scratch of gemm_tn_ex_noalloc (GEMM_TN_NOALLOC_
 # SCRATCH_BYTES in include/gemm_tn.h)
-NOALLOC_SCRATCH_BYTES = 16 * 1024 * 1024
+NOALLOC_SCRATCH_BYTES = 64 * 1024 * 1024
 
 # torch bundles its own HIP runtime under the same soname as the system one
 # (libamdhip64.so.7).  Whichever is loaded first serves the whole process, so

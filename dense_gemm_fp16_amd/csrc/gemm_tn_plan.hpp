@@ -93,6 +93,101 @@ constexpr int64_t kOneKMinTiles = 512;  // fewer tiles: one per workgroup
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Cost model for long-K problems whose 256 tiles number fewer than the CUs
+// (TN operands, 16-byte loads, M and N of at least 256, K of at least
+// kModelMinK): the estimated time, in microseconds, of a tile and split-K
+// choice.  A workgroup costs kKtileUs[tile] per k-tile of its slice plus
+// kFixedUs[tile] (its first loads and its epilogue); the 64 tile's split-K
+// slices run on another kernel (four stages of 64-deep k-tiles), at
+// kKtileUs64Split.  On the 256 tile (one workgroup per CU) a wave costs
+// one workgroup's time, and a last wave holding a fraction f of the CUs'
+// workgroups kShortWave[tile] + (1 - kShortWave[tile]) * f of it: with
+// fewer CUs busy the chip holds a higher clock.  On the 128 and 64 tiles
+// (two per CU) a CU holding L workgroups takes L / 2 workgroup times, plus
+// kShortWave[tile] of one for an odd L (a workgroup alone on its CU).  A
+// split adds kReduceUs (the reduction's launch) and writes and reads back
+// its fp32 partials at kPartialBytesPerUs.  Fitted (least squares on the
+// log of the time) to interleaved timings of 426 tile / split choices on 21
+// shapes from 256^2 x 16384 to 3072^2 x 4096.  Timed again with
+// `bench.py --plan-grid`, the least estimate's choice is 1.3 % slower than
+// the fastest on average over those shapes (20 % at worst, 1024^2 x 4096),
+// and as fast as the fastest on 11 other shapes up to 3072^2 x 8192; the
+// rules used before were 19 % and 31 % slower on average (62 % and 128 %
+// at worst).
+constexpr int64_t kModelMinK = 2048;
+constexpr int64_t kModelMinSliceK = 512;   // eight k-tiles per slice at least
+constexpr int64_t kModelMaxSplits = 64;
+constexpr double kKtileUs[NUM_TILES] = {1.119, 0.750, 0.374};
+constexpr double kKtileUs64Split = 0.304;
+constexpr double kFixedUs[NUM_TILES] = {5.43, 3.15, 1.74};
+constexpr double kShortWave[NUM_TILES] = {0.807, 0.696, 0.733};
+constexpr double kReduceUs = 7.76;
+constexpr double kPartialBytesPerUs = 8.01e6;
+// Largest split-K workspace the model plans for: the fixed scratch of the
+// no-allocation entry point, so that both entry points plan alike.
+constexpr int64_t kModelMaxPartialBytes = GEMM_TN_NOALLOC_SCRATCH_BYTES;
+
+// Bytes of fp32 partials a split into `splits` slices writes (rows padded
+// to four elements, as the workspace lays them out).
+inline int64_t partial_bytes(int64_t batch, int64_t M, int64_t N,
+                             int64_t splits)
+{
+    return splits * batch * M * (cdiv(N, 4) * 4) * 4;
+}
+
+inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
+                          int64_t K, int64_t splits)
+{
+    const int64_t dim = kTileDim[tile];
+    const int64_t ktiles = cdiv(cdiv(K, splits), kBK);
+    const int64_t slices = cdiv(K, ktiles * kBK);
+    const int64_t wgs = cdiv(M, dim) * cdiv(N, dim) * batch * slices;
+    const double per_k = tile == TILE_64 && slices > 1 ? kKtileUs64Split
+                                                        : kKtileUs[tile];
+    const double wg_us = (double)ktiles * per_k + kFixedUs[tile];
+    double waves;
+    if (kTileWgsPerCu[tile] == 1) {
+        waves = (double)(wgs / kCUs);
+        if (wgs % kCUs != 0)
+            waves += kShortWave[tile] + (1.0 - kShortWave[tile]) *
+                                            (double)(wgs % kCUs) / kCUs;
+    } else {
+        const int64_t per_cu = cdiv(wgs, kCUs);
+        waves = (double)(per_cu / 2) + (per_cu % 2 ? kShortWave[tile] : 0.0);
+    }
+    double us = waves * wg_us;
+    if (slices > 1)
+        us += kReduceUs + 2.0 * (double)partial_bytes(batch, M, N, slices) /
+                              kPartialBytesPerUs;
+    return us;
+}
+
+// Tile and split-K factor of least estimated time.  Splits are tried while
+// the slices keep kModelMinSliceK and the partials fit in
+// kModelMaxPartialBytes; a factor that rounds to the slices of a smaller one
+// is skipped.
+inline void choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
+                           int *tile, int64_t *splits)
+{
+    double best = estimate_us(TILE_256, batch, M, N, K, 1);
+    *tile = TILE_256;
+    *splits = 1;
+    for (int t = 0; t < NUM_TILES; ++t)
+        for (int64_t s = 1; s <= kModelMaxSplits && s * kModelMinSliceK <= K;
+             ++s) {
+            if (cdiv(K, cdiv(cdiv(K, s), kBK) * kBK) != s)
+                continue;
+            if (s > 1 && partial_bytes(batch, M, N, s) > kModelMaxPartialBytes)
+                break;
+            const double us = estimate_us(t, batch, M, N, K, s);
+            if (us < best) {
+                best = us;
+                *tile = t;
+                *splits = s;
+            }
+        }
+}
+
 inline bool mul_ok(int64_t a, int64_t b, int64_t *out)
 {
     return !__builtin_mul_overflow(a, b, out);
@@ -287,6 +382,14 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         while (!has_kernel(tile) && tile + 1 < NUM_TILES)
             ++tile;
     }
+    // Long K on TN operands whose 256 tiles would leave CUs idle: tile and
+    // split-K factor from the cost model (a forced tile, split or tail split
+    // keeps the rules above and below).
+    int64_t model_splits = 0;
+    if (o.tile < 0 && o.split < 1 && o.tail < 1 &&
+        loader == PLAN_LOAD_DIRECT && layout == 0 && M >= 256 && N >= 256 &&
+        K >= kModelMinK && tiles(TILE_256) < kCUs)
+        choose_by_cost(batch, M, N, K, &tile, &model_splits);
     // K within one k-tile, many tiles, 16-byte loads and stores: the
     // persistent one-k-tile kernel (128 x 128 tiles), which keeps the next
     // tile's operands in flight while a tile's results are written.
@@ -318,11 +421,15 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     p.tiles_n = (int)cdiv(N, p.bn);
     const int64_t ntiles = (int64_t)p.tiles_m * p.tiles_n * batch;
 
-    // Split K when the tiles alone leave CUs idle and K is long: aim for two
-    // workgroups per CU, with at least four k-tiles per slice.
+    // Split K when the tiles alone leave CUs idle and K is long: as many
+    // slices as one wave of the tile holds (at least four k-tiles each).
     int64_t splits = 1;
-    if (ntiles < kCUs && K >= 1024)
-        splits = cdiv(2 * kCUs, ntiles);
+    if (model_splits > 0)
+        splits = model_splits;
+    else if (ntiles < kCUs && K >= 1024) {
+        const int64_t wave = (int64_t)kCUs * kTileWgsPerCu[tile];
+        splits = wave / ntiles > 1 ? wave / ntiles : 1;
+    }
     if (o.split >= 1)
         splits = o.split;
     else if (o.tail >= 1)

@@ -94,8 +94,10 @@ typedef enum gemm_tn_status {
                                     GEMM_TN_NOALLOC_SCRATCH_BYTES */
 } gemm_tn_status;
 
-/* Size of the fixed per-GPU scratch of gemm_tn_ex_noalloc (16 MiB). */
-#define GEMM_TN_NOALLOC_SCRATCH_BYTES (16 * 1024 * 1024)
+/* Size of the fixed per-GPU scratch of gemm_tn_ex_noalloc (64 MiB): the
+   most partials any plan of the library's own choosing writes (one wave of
+   256 x 256 fp32 tiles), so only a forced plan can need more. */
+#define GEMM_TN_NOALLOC_SCRATCH_BYTES (64 * 1024 * 1024)
 
 /*
  * One GEMM.  M, N, K >= 0.
@@ -168,7 +170,9 @@ int gemm_tn_ex(int64_t batch, int64_t M, int64_t N, int64_t K, float alpha,
  * held until the process ends; it calls no hipMalloc or hipFree.
  *   - A problem whose plan needs more partials than that (splits x batch x
  *     M x round_up(N, 4) x 4 bytes, or the tail rows' share) returns
- *     GEMM_TN_ERR_SCRATCH and launches nothing.
+ *     GEMM_TN_ERR_SCRATCH and launches nothing.  The library's own plans
+ *     never do; a plan forced through the GEMM_TN_FORCE environment
+ *     variable (a tuning override read on every call) can.
  *   - Every call on one GPU shares that GPU's array: calls that overlap on
  *     one GPU (several streams or host threads at once) race on it, and
  *     the caller must order them.  Nothing in it has to start at zero: each

@@ -244,7 +244,7 @@ def test_tail_split_plans(monkeypatch):
                   (64, 1024, 1024, 64), (1, 128, 4096, 8192)]:
         assert describe(*shape)["tail_rows"] == "0", shape
     # tiles with two workgroups per CU take no tail split by themselves
-    p = describe(1, 3072, 3072, 3072)
+    p = describe(1, 3072, 3072, 1024)
     assert p["tile"].startswith("128x128x") and p["tail_rows"] == "0"
     # too short a K for two slices of four k-tiles: no tail split
     assert describe(1, 4352, 4352, 448)["tail_rows"] == "0"
@@ -255,6 +255,82 @@ def test_tail_split_plans(monkeypatch):
     assert (p["tail_rows"], p["tail_split"]) == ("2", "3")
     assert p["grid"] == str((10 - 2) * 5 * 2)
     assert p["tail_grid"] == str(2 * 5 * 2 * 3)
+
+
+def _plan(shape, out="f16"):
+    p = describe(*shape, 0.0, out)
+    return int(p["tile"].split("x")[0]), int(p["split"])
+
+
+def test_cost_model_plans(monkeypatch):
+    """Long K (>= 2048) on TN operands whose 256 tiles would leave CUs
+    idle: the tile and split-K factor of least estimated time.  Each pin is
+    the fastest of the tile x split choices timed on that shape."""
+    # 144 or 225 tiles of 256: one partial wave of whole tiles, not the
+    # 128 tile (3072^2 x 4096: 76 against 93 us) nor a split of the 256
+    # tile into more workgroups than CUs (3840^2 x 4096: 90 against 150 us)
+    assert _plan((1, 3072, 3072, 4096)) == (256, 1)
+    assert _plan((1, 3840, 3840, 4096)) == (256, 1)
+    # 64 tiles of 256 over K = 8192: four slices fill one wave
+    assert _plan((1, 2048, 2048, 8192)) == (256, 4)
+    # 2048^2 x 4096: 256 tiles of 128, one per CU, no split
+    assert _plan((1, 2048, 2048, 4096)) == (128, 1)
+    # 144 tiles of 128 in three slices (51.5 against 81 us on 64 tiles)
+    assert _plan((1, 1536, 1536, 8192)) == (128, 3)
+    # 144 tiles of 64 in three slices
+    assert _plan((1, 768, 768, 4096)) == (64, 3)
+    # 4096^3 (256 tiles of 256) and larger keep the whole-tile plan and its
+    # tail split; the six workloads keep theirs (test_plans_for_the_workloads)
+    assert _plan((1, 4096, 4096, 4096)) == (256, 1)
+    assert describe(1, 4352, 4352, 4096)["tail_rows"] == "2"
+    # outside the model: K below 2048, operands stored along M, an element
+    # loader (K % 8 != 0), M below 256; and any forced tile or split
+    assert _plan((1, 3072, 3072, 1024)) == (128, 1)
+    assert describe(1, 3072, 3072, 4096, layouts=(1, 0))["tile"] \
+        .startswith("128x128x")
+    assert describe(1, 1500, 1700, 4100)["loader"] == "elem"
+    assert _plan((1, 128, 4096, 8192), "f32") == (64, 4)
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=128")
+    assert _plan((1, 3072, 3072, 4096)) == (128, 1)
+    monkeypatch.setenv("GEMM_TN_FORCE", "split=2")
+    assert _plan((1, 3072, 3072, 4096))[1] == 2
+
+
+def test_split_rule_fills_one_wave():
+    """Outside the cost model a split fills one wave of the tile: as many
+    slices as the CUs hold workgroups of it (one per CU for the 256 tile,
+    two for the others), never more."""
+    # 196 tiles of 256 (operands along M, so no cost model; K = 4096):
+    # one wave holds them whole, no split (on TN operands three slices, as
+    # the rule once chose, took 142 us against 80)
+    p = describe(1, 3584, 3584, 4096, layouts=(1, 0))
+    assert p["tile"].startswith("256x256x") and p["split"] == "1"
+    # 165 tiles of 64 (element loader): 3 slices = 495 workgroups <= 512
+    p = describe(1, 700, 900, 4100)
+    assert p["tile"].startswith("64x64x") and p["split"] == "3"
+    # the skinny workload: 128 tiles of 64, 4 slices = 512
+    assert describe(1, 128, 4096, 8192, 0.0, "f32")["split"] == "4"
+
+
+def test_planned_partials_fit_the_noalloc_scratch():
+    """No plan of the planner's own writes more split-K partials than the
+    no-allocation entry point's fixed scratch holds, so both entry points
+    run the same plan: a split fills at most one wave of 256 x 256 fp32
+    tiles, and the cost model skips splits beyond the scratch."""
+    limit = g.NOALLOC_SCRATCH_BYTES
+    for M in (256, 700, 1024, 1536, 2000, 2304, 3000, 3840, 4352, 6144):
+        for N in (256, 1030, 2048, 3333, 4096, 8192):
+            for K in (2048, 8192, 65536):
+                p = describe(1, M, N, K, 0.0, "f32")
+                ws_ld = (N + 3) // 4 * 4
+                split, tail = int(p["split"]), int(p["tail_rows"])
+                if split > 1:
+                    assert split * M * ws_ld * 4 <= limit, (M, N, K, p)
+                if tail:
+                    bm = int(p["tile"].split("x")[0])
+                    tail_m = M - (-(-M // bm) - tail) * bm
+                    assert int(p["tail_split"]) * tail_m * ws_ld * 4 <= \
+                        limit, (M, N, K, p)
 
 
 def test_four_wave_plans(monkeypatch):
@@ -375,12 +451,13 @@ def test_f16acc_broadcast_strides_are_accepted_by_the_checks():
     assert _acc(batch=0, sA=0, sB=0) == OK
 
 
-def test_noalloc_rejects_plans_beyond_its_scratch():
+def test_noalloc_rejects_plans_beyond_its_scratch(monkeypatch):
     """gemm_tn_ex_noalloc refuses, before any launch, a problem whose
-    split-K partials exceed its fixed scratch: the tail split of 4352^2 x
-    4096 needs 4 slices x 512 rows x 4352 x 4 bytes = 35.7 MB > 16 MiB."""
-    M = N = 4352
-    K = 4096
+    split-K partials exceed its fixed scratch.  The planner's own plans
+    stay within it (one wave of 256 x 256 fp32 tiles at most: 64 MiB); a
+    forced 8-way split of 4096^2 x 4096 needs 8 x 64 MiB."""
+    M = N = K = 4096
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256,split=8")
     st = g.gemm_tn_ex_noalloc(1, M, N, K, 1.0, P, K, M * K, P, K, N * K, 0.0,
                               NULL, N, M * N, P, N, M * N, F32, S)
     assert st == g.ERR_SCRATCH

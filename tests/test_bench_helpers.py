@@ -131,3 +131,26 @@ def test_summarize_trace_all_finds_each_configuration(tmp_path):
     assert by["c4b_skinny"][4].strip() == "10.03"
     assert "12.5" in by["c4b_skinny"][10] and "0.7 (16)" in by["c4b_skinny"][11]
     assert by["c1_256"][10].strip() == "-"
+
+
+def test_summarize_plan_grid_compares_the_planner_with_the_fastest(tmp_path):
+    import json
+    p = tmp_path / "grid.jsonl"
+    p.write_text("\n".join([
+        "not a record",
+        json.dumps({"shape": [1, 1024, 1024, 8192], "rounds": 4, "burst": 10,
+                    "planner": {"tile": 128, "split": 4, "us": 29.3},
+                    "choices": [[64, 1, 37.9], [128, 4, 29.0],
+                                [256, 8, 31.0]]}),
+        json.dumps({"shape": [2, 512, 512, 4096], "rounds": 4, "burst": 10,
+                    "planner": {"tile": 64, "split": 1, "us": 20.0},
+                    "choices": [[64, 1, 20.0], [64, 2, 16.0]]})]) + "\n")
+    md = bench.summarize_plan_grid(str(p))
+    lines = md.splitlines()
+    # the planner's time is the grid's time of the same choice
+    assert "| 1x1024x1024x8192 | 128 / 4 | 29.00 | 128 / 4 | 29.00 | 1.000 |" \
+        in lines
+    assert "| 2x512x512x4096 | 64 / 1 | 20.00 | 64 / 2 | 16.00 | 1.250 |" \
+        in lines
+    assert lines[-1] == ("planner / fastest: mean 1.125, max 1.250 over 2 "
+                         "shapes")

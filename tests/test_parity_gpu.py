@@ -603,6 +603,36 @@ def test_tail_split(spec, monkeypatch):
         assert res.ok, f"{spec} {batch}x{M}x{N}x{K}: {res}"
 
 
+# (batch, M, N, K, out, alpha, beta, tile, split the cost model picks)
+COST_MODEL_CASES = [
+    (1, 768, 768, 4096, "f32", 1.0, 0.0, 64, 3),
+    (2, 1000, 1100, 4096, "f16", 0.5, 0.0, 128, 3),     # 16-byte stores off
+    (1, 1000, 1000, 16000, "f32", 1.0, -1.0, 128, 8),
+    (1, 300, 3000, 8192, "f32", 2.0, 0.0, 64, 2),
+    (1, 2000, 2100, 8200, "f16", 1.0, 0.5, 256, 3),     # eight waves
+    (1, 2000, 2100, 8200, "f32", 1.0, 0.5, 256, 3),     # four waves
+    (1, 3072, 3072, 2048, "f16", 1.0, 0.0, 256, 1),     # a partial wave
+]
+
+
+@pytest.mark.parametrize("case", COST_MODEL_CASES)
+def test_cost_model_plans_bit_exact(case):
+    """The plans the cost model picks for long K (every tile, split and
+    unsplit, ragged M, N and K, with and without C), every element bit for
+    bit on integer inputs."""
+    batch, M, N, K, out, alpha, beta, tile, split = case
+    g = _gpu()
+    desc = dict(kv.split("=") for kv in
+                g.describe(batch, M, N, K, beta, out).split())
+    assert desc["tile"].startswith(f"{tile}x") and \
+        desc["split"] == str(split), desc
+    w = _int_workload(batch, M, N, K, out, alpha=alpha, beta=beta)
+    _say(f"[model] {batch}x{M}x{N}x{K} {out}: {desc['tile']} split {split}")
+    d = run_gpu(w)
+    res = full_check(w, d, exact=True)
+    assert res.ok, f"{case}: {res}"
+
+
 def test_tail_split_chosen_by_the_planner():
     """4352^3 leaves a tail of 33 tiles of 256 after one wave: the planner
     splits the last two tile rows 4 ways; every element checked."""
@@ -642,10 +672,10 @@ def test_four_wave_kernel_long_k(K, monkeypatch):
     """The four-wave 256 tile over 1024 k-tiles: whole tiles take the loads
     with the k offset in the scalar offset (K = 2^16), a K tail the per-lane
     form; values in {-1, 0, 1} keep every sum exact."""
-    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256")
+    monkeypatch.setenv("GEMM_TN_FORCE", "tile=256,split=1")
     M = N = 256
     desc = _gpu().describe(1, M, N, K, 0.0, "f32")
-    assert "sched=four-wave" in desc, desc
+    assert "sched=four-wave" in desc and "split=1" in desc.split(), desc
     w = si.build("longk", 1, M, N, K, 1.0, 0.0, "f32", "int", 0x5EED0A02)
     w.A = (w.A.astype(np.float32) // 2).clip(-1, 1).astype(np.float16)
     w.B = (w.B.astype(np.float32) // 2).clip(-1, 1).astype(np.float16)

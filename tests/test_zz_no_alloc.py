@@ -1,7 +1,8 @@
 """gemm_tn_ex_noalloc against gemm_tn_ex on the GPU: the same kernels with
 the split-K partials in the library's fixed per-GPU scratch instead of the
 allocated workspace must give the same bits.  Two calls in a row (the
-second smaller), then a tail-split problem, each compared bit for bit with
+second smaller), then a tail-split problem and two splits of the cost
+model (the last filling the whole scratch), each compared bit for bit with
 gemm_tn_ex on the same inputs."""
 import numpy as np
 import pytest
@@ -30,10 +31,12 @@ def _run(g, fn, w, D):
 
 
 # (M, N, K, plan the planner must choose): the skinny workload (4 slices,
-# 8 MiB of partials), a smaller split (16 slices, 8 MiB), and a tail split
-# (the bottom tile row in 3 slices, 12.6 MB)
+# 8 MiB of partials), a smaller split (16 slices, 8 MiB), a tail split
+# (the bottom tile row in 3 slices, 12.6 MB), and splits of the cost model
+# (3 slices of 1536^2, 27 MiB; 16 slices of 1024^2, the whole 64 MiB)
 CASES = [(128, 4096, 8192, "split=4"), (64, 2048, 4096, "split=16"),
-         (4352, 4096, 1024, "tail_split=3")]
+         (4352, 4096, 1024, "tail_split=3"), (1536, 1536, 8192, "split=3"),
+         (1024, 1024, 32768, "split=16")]
 
 
 def test_noalloc_matches_gemm_tn_ex():

@@ -93,10 +93,9 @@ constexpr int64_t kOneKMinTiles = 512;  // fewer tiles: one per workgroup
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Cost model for long-K problems whose 256 tiles number fewer than the CUs
-// (TN operands, 16-byte loads, M and N of at least 256, K of at least
-// kModelMinK): the estimated time, in microseconds, of a tile and split-K
-// choice.  A workgroup costs kKtileUs[tile] per k-tile of its slice plus
+// Cost model for problems with K of at least kModelMinK whose 256 tiles
+// number fewer than the CUs (TN operands, 16-byte loads): the estimated
+// time, in microseconds, of a tile and split-K choice.  A workgroup costs kKtileUs[tile] per k-tile of its slice plus
 // kFixedUs[tile] (its first loads and its epilogue); the 64 tile's split-K
 // slices run on another kernel (four stages of 64-deep k-tiles), at
 // kKtileUs64Split.  On the 256 tile (one workgroup per CU) a wave costs
@@ -111,12 +110,17 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // shapes from 256^2 x 16384 to 3072^2 x 4096.  Timed again with
 // `bench.py --plan-grid`, the least estimate's choice is 1.3 % slower than
 // the fastest on average over those shapes (20 % at worst, 1024^2 x 4096),
-// and as fast as the fastest on 11 other shapes up to 3072^2 x 8192; the
-// rules used before were 19 % and 31 % slower on average (62 % and 128 %
-// at worst).
-constexpr int64_t kModelMinK = 2048;
+// as fast as the fastest on 11 other shapes up to 3072^2 x 8192, and 1.3 %
+// slower on 14 shapes with K of 1024 or 1536 or M below 256 (11 % at
+// worst); the rules used before were 19 %, 31 % and 10 % slower on average
+// (62 %, 128 % and 58 % at worst).
+constexpr int64_t kModelMinK = 1024;
 constexpr int64_t kModelMinSliceK = 512;   // eight k-tiles per slice at least
-constexpr int64_t kModelMaxSplits = 64;
+// Split factors tried: every one to 16, then about four per octave to 512.
+constexpr int kModelSplits[] = {1,  2,  3,  4,   5,   6,   7,   8,   9,
+                                10, 11, 12, 13,  14,  15,  16,  20,  24,
+                                28, 32, 40, 48,  56,  64,  80,  96,  112,
+                                128, 160, 192, 224, 256, 320, 384, 448, 512};
 constexpr double kKtileUs[NUM_TILES] = {1.119, 0.750, 0.374};
 constexpr double kKtileUs64Split = 0.304;
 constexpr double kFixedUs[NUM_TILES] = {5.43, 3.15, 1.74};
@@ -162,19 +166,21 @@ inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
     return us;
 }
 
-// Tile and split-K factor of least estimated time.  Splits are tried while
-// the slices keep kModelMinSliceK and the partials fit in
-// kModelMaxPartialBytes; a factor that rounds to the slices of a smaller one
-// is skipped.
+// Tile and split-K factor of least estimated time.  The 256 tile is tried
+// when M and N are at least 256; splits while the slices keep
+// kModelMinSliceK and the partials fit in kModelMaxPartialBytes; a factor
+// that rounds to the slices of a smaller one is skipped.
 inline void choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
                            int *tile, int64_t *splits)
 {
-    double best = estimate_us(TILE_256, batch, M, N, K, 1);
-    *tile = TILE_256;
+    const int first = M >= 256 && N >= 256 ? TILE_256 : TILE_128;
+    double best = estimate_us(first, batch, M, N, K, 1);
+    *tile = first;
     *splits = 1;
-    for (int t = 0; t < NUM_TILES; ++t)
-        for (int64_t s = 1; s <= kModelMaxSplits && s * kModelMinSliceK <= K;
-             ++s) {
+    for (int t = first; t < NUM_TILES; ++t)
+        for (const int s : kModelSplits) {
+            if (s > 1 && s * kModelMinSliceK > K)
+                break;
             if (cdiv(K, cdiv(cdiv(K, s), kBK) * kBK) != s)
                 continue;
             if (s > 1 && partial_bytes(batch, M, N, s) > kModelMaxPartialBytes)
@@ -382,13 +388,13 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         while (!has_kernel(tile) && tile + 1 < NUM_TILES)
             ++tile;
     }
-    // Long K on TN operands whose 256 tiles would leave CUs idle: tile and
-    // split-K factor from the cost model (a forced tile, split or tail split
-    // keeps the rules above and below).
+    // K of 1024 or more on TN operands whose 256 tiles would leave CUs
+    // idle: tile and split-K factor from the cost model (a forced tile,
+    // split or tail split keeps the rules above and below).
     int64_t model_splits = 0;
     if (o.tile < 0 && o.split < 1 && o.tail < 1 &&
-        loader == PLAN_LOAD_DIRECT && layout == 0 && M >= 256 && N >= 256 &&
-        K >= kModelMinK && tiles(TILE_256) < kCUs)
+        loader == PLAN_LOAD_DIRECT && layout == 0 && K >= kModelMinK &&
+        tiles(TILE_256) < kCUs)
         choose_by_cost(batch, M, N, K, &tile, &model_splits);
     // K within one k-tile, many tiles, 16-byte loads and stores: the
     // persistent one-k-tile kernel (128 x 128 tiles), which keeps the next

@@ -244,7 +244,7 @@ def test_tail_split_plans(monkeypatch):
                   (64, 1024, 1024, 64), (1, 128, 4096, 8192)]:
         assert describe(*shape)["tail_rows"] == "0", shape
     # tiles with two workgroups per CU take no tail split by themselves
-    p = describe(1, 3072, 3072, 1024)
+    p = describe(1, 3072, 3072, 512)
     assert p["tile"].startswith("128x128x") and p["tail_rows"] == "0"
     # too short a K for two slices of four k-tiles: no tail split
     assert describe(1, 4352, 4352, 448)["tail_rows"] == "0"
@@ -263,7 +263,7 @@ def _plan(shape, out="f16"):
 
 
 def test_cost_model_plans(monkeypatch):
-    """Long K (>= 2048) on TN operands whose 256 tiles would leave CUs
+    """K of 1024 or more on TN operands whose 256 tiles would leave CUs
     idle: the tile and split-K factor of least estimated time.  Each pin is
     the fastest of the tile x split choices timed on that shape."""
     # 144 or 225 tiles of 256: one partial wave of whole tiles, not the
@@ -279,17 +279,25 @@ def test_cost_model_plans(monkeypatch):
     assert _plan((1, 1536, 1536, 8192)) == (128, 3)
     # 144 tiles of 64 in three slices
     assert _plan((1, 768, 768, 4096)) == (64, 3)
+    # K of 1024: 144 whole tiles of 256 (25.2 against 28.0 us on the 128
+    # tile); 512^2 x 1024 unsplit (6.0 against 9.5 us in four slices)
+    assert _plan((1, 3072, 3072, 1024)) == (256, 1)
+    assert _plan((1, 512, 512, 1024)) == (64, 1)
+    # M below 256: no 256 tile; the skinny workload keeps its 4 slices
+    assert _plan((1, 192, 6144, 8192)) == (128, 5)
+    assert _plan((1, 128, 4096, 8192), "f32") == (64, 4)
+    # a tiny output over the longest K: 512 slices of 4096
+    assert _plan((1, 16, 24, 2 ** 21), "f32") == (64, 512)
     # 4096^3 (256 tiles of 256) and larger keep the whole-tile plan and its
     # tail split; the six workloads keep theirs (test_plans_for_the_workloads)
     assert _plan((1, 4096, 4096, 4096)) == (256, 1)
     assert describe(1, 4352, 4352, 4096)["tail_rows"] == "2"
-    # outside the model: K below 2048, operands stored along M, an element
-    # loader (K % 8 != 0), M below 256; and any forced tile or split
-    assert _plan((1, 3072, 3072, 1024)) == (128, 1)
+    # outside the model: K below 1024, operands stored along M, an element
+    # loader (K % 8 != 0); and any forced tile or split
+    assert _plan((1, 3072, 3072, 512)) == (128, 1)
     assert describe(1, 3072, 3072, 4096, layouts=(1, 0))["tile"] \
         .startswith("128x128x")
     assert describe(1, 1500, 1700, 4100)["loader"] == "elem"
-    assert _plan((1, 128, 4096, 8192), "f32") == (64, 4)
     monkeypatch.setenv("GEMM_TN_FORCE", "tile=128")
     assert _plan((1, 3072, 3072, 4096)) == (128, 1)
     monkeypatch.setenv("GEMM_TN_FORCE", "split=2")

@@ -317,7 +317,8 @@ def time_vendor_interleaved(w, rounds=6, burst=10):
     return {k: statistics.median(v) for k, v in times.items()}
 
 
-PLAN_GRID_SPLITS = (1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32, 48, 64)
+PLAN_GRID_SPLITS = (1, 2, 3, 4, 5, 6, 8, 10, 12, 16, 24, 32, 48, 64, 96, 128,
+                    192, 256)
 PLAN_GRID_SHAPES = (
     "1x512x512x2048,1x512x512x8192,1x768x768x4096,1x1024x1024x2048,"
     "1x1024x1024x4096,1x1024x1024x8192,1x1024x1024x16384,1x1536x1536x2048,"

@@ -95,25 +95,28 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Cost model for problems with K of at least kModelMinK whose 256 tiles
 // number fewer than the CUs (TN operands, 16-byte loads): the estimated
-// time, in microseconds, of a tile and split-K choice.  A workgroup costs kKtileUs[tile] per k-tile of its slice plus
-// kFixedUs[tile] (its first loads and its epilogue); the 64 tile's split-K
-// slices run on another kernel (four stages of 64-deep k-tiles), at
-// kKtileUs64Split.  On the 256 tile (one workgroup per CU) a wave costs
-// one workgroup's time, and a last wave holding a fraction f of the CUs'
-// workgroups kShortWave[tile] + (1 - kShortWave[tile]) * f of it: with
-// fewer CUs busy the chip holds a higher clock.  On the 128 and 64 tiles
-// (two per CU) a CU holding L workgroups takes L / 2 workgroup times, plus
-// kShortWave[tile] of one for an odd L (a workgroup alone on its CU).  A
-// split adds kReduceUs (the reduction's launch) and writes and reads back
-// its fp32 partials at kPartialBytesPerUs.  Fitted (least squares on the
-// log of the time) to interleaved timings of 426 tile / split choices on 21
-// shapes from 256^2 x 16384 to 3072^2 x 4096.  Timed again with
-// `bench.py --plan-grid`, the least estimate's choice is 1.3 % slower than
-// the fastest on average over those shapes (20 % at worst, 1024^2 x 4096),
-// as fast as the fastest on 11 other shapes up to 3072^2 x 8192, and 1.3 %
-// slower on 14 shapes with K of 1024 or 1536 or M below 256 (11 % at
-// worst); the rules used before were 19 %, 31 % and 10 % slower on average
-// (62 %, 128 % and 58 % at worst).
+// time, in microseconds, of a tile and split-K choice.
+//   - A workgroup costs kKtileUs[tile] per k-tile of its slice plus
+//     kFixedUs[tile] (its first loads and its epilogue); the 64 tile's
+//     split-K slices run on another kernel (four stages of 64-deep
+//     k-tiles), at kKtileUs64Split per k-tile.
+//   - On the 256 tile (one workgroup per CU) a wave costs one workgroup's
+//     time, and a last wave holding a fraction f of the CUs' workgroups
+//     kShortWave[tile] + (1 - kShortWave[tile]) * f of it: with fewer CUs
+//     busy the chip holds a higher clock.
+//   - On the 128 and 64 tiles (two per CU) a CU holding L workgroups takes
+//     L / 2 workgroup times, plus kShortWave[tile] of one for an odd L (a
+//     workgroup alone on its CU).
+//   - A split adds kReduceUs (the reduction's launch), kReduceSliceUs per
+//     slice (each reduction thread reads the slices eight at a time), and
+//     the write and read-back of its fp32 partials at kPartialBytesPerUs.
+// The constants are a least-squares fit, on the log of the time, to 886
+// timed tile / split choices on 42 shapes from 64^2 x 65536 to 3072^2 x
+// 4096.  Timed again with `bench.py --plan-grid`, the least estimate's
+// choice is 3.0 % slower than the fastest on average over those shapes (30 %
+// at worst, 16 x 128^2 x 8192), and 0.2 % slower over 20 other shapes up to
+// 3072^2 x 8192 (2.2 % at worst); the rules used before were 17 % and 25 %
+// slower on average (70 % and 117 % at worst).
 constexpr int64_t kModelMinK = 1024;
 constexpr int64_t kModelMinSliceK = 512;   // eight k-tiles per slice at least
 // Split factors tried: every one to 16, then about four per octave to 512.
@@ -121,12 +124,13 @@ constexpr int kModelSplits[] = {1,  2,  3,  4,   5,   6,   7,   8,   9,
                                 10, 11, 12, 13,  14,  15,  16,  20,  24,
                                 28, 32, 40, 48,  56,  64,  80,  96,  112,
                                 128, 160, 192, 224, 256, 320, 384, 448, 512};
-constexpr double kKtileUs[NUM_TILES] = {1.119, 0.750, 0.374};
-constexpr double kKtileUs64Split = 0.304;
-constexpr double kFixedUs[NUM_TILES] = {5.43, 3.15, 1.74};
-constexpr double kShortWave[NUM_TILES] = {0.807, 0.696, 0.733};
-constexpr double kReduceUs = 7.76;
-constexpr double kPartialBytesPerUs = 8.01e6;
+constexpr double kKtileUs[NUM_TILES] = {1.250, 0.805, 0.384};
+constexpr double kKtileUs64Split = 0.357;
+constexpr double kFixedUs[NUM_TILES] = {5.88, 3.64, 1.57};
+constexpr double kShortWave[NUM_TILES] = {0.739, 0.665, 0.729};
+constexpr double kReduceUs = 5.48;
+constexpr double kReduceSliceUs = 0.0888;
+constexpr double kPartialBytesPerUs = 8.40e6;
 // Largest split-K workspace the model plans for: the fixed scratch of the
 // no-allocation entry point, so that both entry points plan alike.
 constexpr int64_t kModelMaxPartialBytes = GEMM_TN_NOALLOC_SCRATCH_BYTES;
@@ -161,8 +165,9 @@ inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
     }
     double us = waves * wg_us;
     if (slices > 1)
-        us += kReduceUs + 2.0 * (double)partial_bytes(batch, M, N, slices) /
-                              kPartialBytesPerUs;
+        us += kReduceUs + kReduceSliceUs * (double)slices +
+              2.0 * (double)partial_bytes(batch, M, N, slices) /
+                  kPartialBytesPerUs;
     return us;
 }
 

@@ -286,8 +286,8 @@ def test_cost_model_plans(monkeypatch):
     # M below 256: no 256 tile; the skinny workload keeps its 4 slices
     assert _plan((1, 192, 6144, 8192)) == (128, 5)
     assert _plan((1, 128, 4096, 8192), "f32") == (64, 4)
-    # a tiny output over the longest K: 512 slices of 4096
-    assert _plan((1, 16, 24, 2 ** 21), "f32") == (64, 512)
+    # a tiny output over the longest K: 256 slices of 8192
+    assert _plan((1, 16, 24, 2 ** 21), "f32") == (64, 256)
     # 4096^3 (256 tiles of 256) and larger keep the whole-tile plan and its
     # tail split; the six workloads keep theirs (test_plans_for_the_workloads)
     assert _plan((1, 4096, 4096, 4096)) == (256, 1)

@@ -608,7 +608,8 @@ COST_MODEL_CASES = [
     (1, 768, 768, 4096, "f32", 1.0, 0.0, 64, 3),
     (2, 1000, 1100, 4096, "f16", 0.5, 0.0, 128, 3),     # 16-byte stores off
     (1, 1000, 1000, 16000, "f32", 1.0, -1.0, 128, 8),
-    (1, 300, 3000, 8192, "f32", 2.0, 0.0, 64, 2),
+    (1, 300, 3000, 8192, "f32", 2.0, 0.0, 128, 7),
+    (1, 320, 320, 24576, "f32", 1.0, 0.5, 64, 20),     # 20 slices: 8 + 8 + 3
     (1, 2000, 2100, 8200, "f16", 1.0, 0.5, 256, 3),     # eight waves
     (1, 2000, 2100, 8200, "f32", 1.0, 0.5, 256, 3),     # four waves
     (1, 3072, 3072, 2048, "f16", 1.0, 0.0, 256, 1),     # a partial wave

@@ -341,9 +341,10 @@ def plan_grid(shapes, rounds=4, burst=10):
     def cdiv(x, y):
         return -(-x // y)
 
-    def plan_of(b, M, N, K):
+    def plan_of(b, M, N, K, tail=False):
         d = dict(kv.split("=") for kv in g.describe(b, M, N, K).split())
-        return int(d["tile"].split("x")[0]), int(d["split"])
+        p = (int(d["tile"].split("x")[0]), int(d["split"]))
+        return p + (int(d["tail_rows"]), int(d["tail_split"])) if tail else p
 
     gen = torch.Generator(device="cuda")
     for tok in shapes.split(","):
@@ -385,7 +386,7 @@ def plan_grid(shapes, rounds=4, burst=10):
                 os.environ["GEMM_TN_FORCE"] = spec
                 assert plan_of(b, M, N, K) == key, (tok, key)
             os.environ["GEMM_TN_FORCE"] = ""
-            chosen = plan_of(b, M, N, K)
+            chosen = plan_of(b, M, N, K, tail=True)
         finally:
             if old is None:
                 os.environ.pop("GEMM_TN_FORCE", None)
@@ -395,6 +396,7 @@ def plan_grid(shapes, rounds=4, burst=10):
         print(json.dumps({
             "shape": [b, M, N, K], "rounds": rounds, "burst": burst,
             "planner": {"tile": chosen[0], "split": chosen[1],
+                        "tail_rows": chosen[2], "tail_split": chosen[3],
                         "us": round(med["planner"], 2)},
             "choices": [[k[0], k[1], round(med[k], 2)] for k in specs]}),
             flush=True)
@@ -403,7 +405,10 @@ def plan_grid(shapes, rounds=4, burst=10):
 
 def summarize_plan_grid(path):
     """Markdown table of a --plan-grid run: per shape the planner's choice
-    and the fastest choice, each with its time, and their ratio."""
+    and the fastest choice, each with its time, and their ratio.  The
+    planner's time is the grid's for the same choice, or its own run's
+    where the grid has no such choice (the grid runs whole tiles without a
+    tail split)."""
     rows, ratios = [], []
     for line in open(path):
         if not line.startswith("{"):
@@ -411,12 +416,15 @@ def summarize_plan_grid(path):
         r = json.loads(line)
         best = min(r["choices"], key=lambda c: c[2])
         p = r["planner"]
+        tail = p.get("tail_rows", 0)
         own = [c for c in r["choices"] if c[0] == p["tile"] and
-               c[1] == p["split"]]
+               c[1] == p["split"]] if not tail else []
         t = own[0][2] if own else p["us"]
         ratios.append(t / best[2])
         b, M, N, K = r["shape"]
-        rows.append(f"| {b}x{M}x{N}x{K} | {p['tile']} / {p['split']} | "
+        name = f"{p['tile']} / {p['split']}" + (
+            f" + tail {tail} x {p['tail_split']}" if tail else "")
+        rows.append(f"| {b}x{M}x{N}x{K} | {name} | "
                     f"{t:.2f} | {best[0]} / {best[1]} | {best[2]:.2f} | "
                     f"{t / best[2]:.3f} |")
     out = ["| batch x M x N x K | planner: tile / split | us | fastest: "

@@ -93,9 +93,9 @@ constexpr int64_t kOneKMinTiles = 512;  // fewer tiles: one per workgroup
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Cost model for problems with K of at least kModelMinK whose 256 tiles
-// number fewer than the CUs (TN operands, 16-byte loads): the estimated
-// time, in microseconds, of a tile and split-K choice.
+// Cost model for problems with K of at least kModelMinK on TN operands with
+// 16-byte loads: the estimated time, in microseconds, of a tile and split-K
+// choice (on the 256 tile unsplit, with its tail split, tail_split_of).
 //   - A workgroup costs kKtileUs[tile] per k-tile of its slice plus
 //     kFixedUs[tile] (its first loads and its epilogue); the 64 tile's
 //     split-K slices run on another kernel (four stages of 64-deep
@@ -113,10 +113,10 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // The constants are a least-squares fit, on the log of the time, to 886
 // timed tile / split choices on 42 shapes from 64^2 x 65536 to 3072^2 x
 // 4096.  Timed again with `bench.py --plan-grid`, the least estimate's
-// choice is 3.0 % slower than the fastest on average over those shapes (30 %
-// at worst, 16 x 128^2 x 8192), and 0.2 % slower over 20 other shapes up to
-// 3072^2 x 8192 (2.2 % at worst); the rules used before were 17 % and 25 %
-// slower on average (70 % and 117 % at worst).
+// choice is 2.9 % slower than the fastest on average over those shapes (18 %
+// at worst, 512^2 x 2048) and as fast as the fastest over 20 other shapes
+// up to 3072^2 x 8192; the rules used before were 17 % and 25 % slower on
+// average (71 % and 111 % at worst).
 constexpr int64_t kModelMinK = 1024;
 constexpr int64_t kModelMinSliceK = 512;   // eight k-tiles per slice at least
 // Split factors tried: every one to 16, then about four per octave to 512.
@@ -143,15 +143,77 @@ inline int64_t partial_bytes(int64_t batch, int64_t M, int64_t N,
     return splits * batch * M * (cdiv(N, 4) * 4) * 4;
 }
 
-inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
-                          int64_t K, int64_t splits)
+// Tail split of a grid of whole tiles.  With whole tiles only, a last wave
+// holding less than half a wave's tiles (a wave: every CU running as many
+// workgroups as fit) leaves most CUs idle for a whole tile's time.  Instead
+// the fewest bottom tile rows that hold that remainder are split along K
+// (at least four k-tiles per slice, at most a wave of workgroups), and the
+// rows above run as whole tiles.  More slices shorten the tail's compute
+// (about a tile's time / slices) but each adds a round trip of fp32
+// partials for every tail tile (written, then read by the reduction): about
+// sqrt(9 * k-tiles / tail tiles) slices balance the two.  Measured on the
+// 256 tile at K = 4096 (interleaved medians): 4352^2, 34 tail tiles: 142.7
+// / 140.7 / 141.5 / 142.7 / 146.2 us for 3 / 4 / 5 / 6 / 7 slices (the
+// formula: 4); 6144^2, 72 tail tiles: 255.8 / 253.8 us for 2 / 3 (the
+// formula: 3).  Taken only for tiles that run one workgroup per CU: where
+// two fit, the last wave's tiles run at twice the speed, and measured on
+// 3072^3 (128 tiles) the extra launch and reduction cost more than the tail
+// they save.  force_rows >= 0 and force_splits >= 2 override the choice;
+// rows = 0 means no tail split.
+struct TailSplit {
+    int rows = 0;
+    int64_t splits = 1;
+    int64_t k_split = 0;
+};
+
+inline TailSplit tail_split_of(int tile, int64_t batch, int64_t tiles_m,
+                               int64_t tiles_n, int64_t K, int force_rows,
+                               int force_splits)
 {
-    const int64_t dim = kTileDim[tile];
-    const int64_t ktiles = cdiv(cdiv(K, splits), kBK);
-    const int64_t slices = cdiv(K, ktiles * kBK);
-    const int64_t wgs = cdiv(M, dim) * cdiv(N, dim) * batch * slices;
-    const double per_k = tile == TILE_64 && slices > 1 ? kKtileUs64Split
-                                                        : kKtileUs[tile];
+    TailSplit t;
+    const int64_t row_tiles = tiles_n * batch;
+    const int64_t ntiles = tiles_m * row_tiles;
+    const int64_t slots = (int64_t)kCUs * kTileWgsPerCu[tile];
+    const int64_t full = ntiles / slots, rem = ntiles % slots;
+    int64_t rows = 0;
+    if (kTileWgsPerCu[tile] == 1 && full >= 1 && rem > 0 && rem <= slots / 2)
+        rows = cdiv(rem, row_tiles);
+    if (force_rows >= 0)
+        rows = force_rows;
+    if (rows <= 0 || rows >= tiles_m)
+        return t;
+    const int64_t tail_tiles = rows * row_tiles;
+    int64_t ts = slots / tail_tiles;
+    const int64_t ktiles = cdiv(K, kBK);
+    int64_t balance = 1;                // round(sqrt(9 * ktiles / tail_tiles))
+    while ((2 * balance + 1) * (2 * balance + 1) * tail_tiles <= 36 * ktiles)
+        ++balance;
+    if (balance < ts)
+        ts = balance;
+    if (force_splits >= 2)
+        ts = force_splits;
+    const int64_t max_splits = K / (4 * kBK) > 1 ? K / (4 * kBK) : 1;
+    if (ts > max_splits)
+        ts = max_splits;
+    if (ts < 2)
+        return t;
+    const int64_t k_split = cdiv(cdiv(K, ts), kBK) * kBK;
+    ts = cdiv(K, k_split);
+    if (ts < 2)
+        return t;
+    t.rows = (int)rows;
+    t.splits = ts;
+    t.k_split = k_split;
+    return t;
+}
+
+// Estimated time of `wgs` workgroups of `ktiles` k-tiles each on `tile`
+// (split_kernel: the split-K instantiation, which differs on the 64 tile).
+inline double waves_us(int tile, int64_t wgs, int64_t ktiles,
+                       bool split_kernel)
+{
+    const double per_k = tile == TILE_64 && split_kernel ? kKtileUs64Split
+                                                          : kKtileUs[tile];
     const double wg_us = (double)ktiles * per_k + kFixedUs[tile];
     double waves;
     if (kTileWgsPerCu[tile] == 1) {
@@ -163,12 +225,44 @@ inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
         const int64_t per_cu = cdiv(wgs, kCUs);
         waves = (double)(per_cu / 2) + (per_cu % 2 ? kShortWave[tile] : 0.0);
     }
-    double us = waves * wg_us;
-    if (slices > 1)
-        us += kReduceUs + kReduceSliceUs * (double)slices +
-              2.0 * (double)partial_bytes(batch, M, N, slices) /
-                  kPartialBytesPerUs;
-    return us;
+    return waves * wg_us;
+}
+
+// Estimated time of the reduction of `slices` slices of `bytes` of partials.
+inline double reduce_us(int64_t slices, int64_t bytes)
+{
+    return kReduceUs + kReduceSliceUs * (double)slices +
+           2.0 * (double)bytes / kPartialBytesPerUs;
+}
+
+// Estimated time of `tile` with K in `splits` slices; with one slice on a
+// tile that takes a tail split (force_tail_rows as in tail_split_of), of
+// the whole tiles above the tail, the tail's slices, and their reduction.
+inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
+                          int64_t K, int64_t splits, int force_tail_rows)
+{
+    const int64_t dim = kTileDim[tile];
+    const int64_t tiles_m = cdiv(M, dim), tiles_n = cdiv(N, dim);
+    const int64_t ntiles = tiles_m * tiles_n * batch;
+    const int64_t ktiles = cdiv(cdiv(K, splits), kBK);
+    const int64_t slices = cdiv(K, ktiles * kBK);
+    if (slices == 1) {
+        const TailSplit t = tail_split_of(tile, batch, tiles_m, tiles_n, K,
+                                          force_tail_rows, -1);
+        if (t.rows > 0) {
+            const int64_t tail_tiles = t.rows * tiles_n * batch;
+            const int64_t tail_m = M - (tiles_m - t.rows) * dim;
+            return waves_us(tile, ntiles - tail_tiles, ktiles, false) +
+                   waves_us(tile, tail_tiles * t.splits,
+                            t.k_split / kBK, true) +
+                   reduce_us(t.splits, t.splits * batch * tail_m *
+                                           (cdiv(N, 4) * 4) * 4);
+        }
+    }
+    return waves_us(tile, ntiles * slices, ktiles, slices > 1) +
+           (slices > 1 ? reduce_us(slices,
+                                   partial_bytes(batch, M, N, slices))
+                       : 0.0);
 }
 
 // Tile and split-K factor of least estimated time.  The 256 tile is tried
@@ -176,10 +270,10 @@ inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
 // kModelMinSliceK and the partials fit in kModelMaxPartialBytes; a factor
 // that rounds to the slices of a smaller one is skipped.
 inline void choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
-                           int *tile, int64_t *splits)
+                           int force_tail_rows, int *tile, int64_t *splits)
 {
     const int first = M >= 256 && N >= 256 ? TILE_256 : TILE_128;
-    double best = estimate_us(first, batch, M, N, K, 1);
+    double best = estimate_us(first, batch, M, N, K, 1, force_tail_rows);
     *tile = first;
     *splits = 1;
     for (int t = first; t < NUM_TILES; ++t)
@@ -190,7 +284,8 @@ inline void choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
                 continue;
             if (s > 1 && partial_bytes(batch, M, N, s) > kModelMaxPartialBytes)
                 break;
-            const double us = estimate_us(t, batch, M, N, K, s);
+            const double us =
+                estimate_us(t, batch, M, N, K, s, force_tail_rows);
             if (us < best) {
                 best = us;
                 *tile = t;
@@ -393,14 +488,13 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         while (!has_kernel(tile) && tile + 1 < NUM_TILES)
             ++tile;
     }
-    // K of 1024 or more on TN operands whose 256 tiles would leave CUs
-    // idle: tile and split-K factor from the cost model (a forced tile,
-    // split or tail split keeps the rules above and below).
+    // K of 1024 or more on TN operands: tile and split-K factor from the
+    // cost model (a forced tile, split or tail split keeps the rules above
+    // and below).
     int64_t model_splits = 0;
     if (o.tile < 0 && o.split < 1 && o.tail < 1 &&
-        loader == PLAN_LOAD_DIRECT && layout == 0 && K >= kModelMinK &&
-        tiles(TILE_256) < kCUs)
-        choose_by_cost(batch, M, N, K, &tile, &model_splits);
+        loader == PLAN_LOAD_DIRECT && layout == 0 && K >= kModelMinK)
+        choose_by_cost(batch, M, N, K, o.tail, &tile, &model_splits);
     // K within one k-tile, many tiles, 16-byte loads and stores: the
     // persistent one-k-tile kernel (128 x 128 tiles), which keeps the next
     // tile's operands in flight while a tile's results are written.
@@ -474,59 +568,16 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
     if (o.group >= 1)
         p.group_m = o.group;
 
-    // Tail split.  With whole tiles only, a last wave holding less than
-    // half a wave's tiles (a wave: every CU running as many workgroups as
-    // fit) leaves most CUs idle for a whole tile's time.  Instead the
-    // fewest bottom tile rows that hold that remainder are split along K
-    // (at least four k-tiles per slice, at most a wave of workgroups), and
-    // the rows above run as whole tiles.  More slices shorten the tail's
-    // compute (about a tile's time / slices) but each adds a round trip of
-    // fp32 partials for every tail tile (written, then read by the
-    // reduction): about sqrt(9 * k-tiles / tail tiles) slices balance the
-    // two.  Measured on the 256 tile at K = 4096 (interleaved medians):
-    // 4352^2, 34 tail tiles: 142.7 / 140.7 / 141.5 / 142.7 / 146.2 us for
-    // 3 / 4 / 5 / 6 / 7 slices (the formula: 4); 6144^2, 72 tail tiles:
-    // 255.8 / 253.8 us for 2 / 3 (the formula: 3).  Chosen only for tiles that
-    // run one workgroup per CU: where two fit, the last wave's tiles run
-    // at twice the speed, and measured on 3072^3 (128 tiles) the extra
-    // launch and reduction cost more than the tail they save.
+    // Tail split (tail_split_of) of a grid of whole tiles.
     const int64_t row_tiles = (int64_t)p.tiles_n * batch;
-    const int64_t slots = (int64_t)kCUs * kTileWgsPerCu[tile];
-    int tail_rows = 0;
     if (p.splits == 1) {
-        const int64_t full = ntiles / slots, rem = ntiles % slots;
-        if (kTileWgsPerCu[tile] == 1 && full >= 1 && rem > 0 &&
-            rem <= slots / 2)
-            tail_rows = (int)cdiv(rem, row_tiles);
-        if (o.tail >= 0)
-            tail_rows = o.tail;
-        if (tail_rows >= p.tiles_m)
-            tail_rows = 0;
-    }
-    if (tail_rows > 0) {
-        const int64_t tail_tiles = tail_rows * row_tiles;
-        int64_t ts = slots / tail_tiles;
-        const int64_t ktiles = cdiv(K, kBK);
-        int64_t balance = 1;            // round(sqrt(9 * ktiles / tail_tiles))
-        while ((2 * balance + 1) * (2 * balance + 1) * tail_tiles <=
-               36 * ktiles)
-            ++balance;
-        if (balance < ts)
-            ts = balance;
-        if (o.tail_split >= 2)
-            ts = o.tail_split;
-        if (ts > max_splits)
-            ts = max_splits;
-        if (ts >= 2) {
-            p.tail_k_split = cdiv(cdiv(K, ts), kBK) * kBK;
-            ts = cdiv(K, p.tail_k_split);
-        }
-        if (ts >= 2) {
-            p.tail_rows = tail_rows;
-            p.tail_splits = (int)ts;
-            p.tail_grid = tail_tiles * ts;
-        } else {
-            p.tail_k_split = 0;
+        const TailSplit t = tail_split_of(tile, batch, p.tiles_m, p.tiles_n,
+                                          K, o.tail, o.tail_split);
+        if (t.rows > 0) {
+            p.tail_rows = t.rows;
+            p.tail_splits = (int)t.splits;
+            p.tail_k_split = t.k_split;
+            p.tail_grid = t.rows * row_tiles * t.splits;
         }
     }
 

@@ -263,9 +263,9 @@ def _plan(shape, out="f16"):
 
 
 def test_cost_model_plans(monkeypatch):
-    """K of 1024 or more on TN operands whose 256 tiles would leave CUs
-    idle: the tile and split-K factor of least estimated time.  Each pin is
-    the fastest of the tile x split choices timed on that shape."""
+    """K of 1024 or more on TN operands: the tile and split-K factor (and,
+    on the 256 tile, the tail split) of least estimated time.  Each pin is
+    the fastest of the choices timed on that shape."""
     # 144 or 225 tiles of 256: one partial wave of whole tiles, not the
     # 128 tile (3072^2 x 4096: 76 against 93 us) nor a split of the 256
     # tile into more workgroups than CUs (3840^2 x 4096: 90 against 150 us)
@@ -288,10 +288,16 @@ def test_cost_model_plans(monkeypatch):
     assert _plan((1, 128, 4096, 8192), "f32") == (64, 4)
     # a tiny output over the longest K: 256 slices of 8192
     assert _plan((1, 16, 24, 2 ** 21), "f32") == (64, 256)
-    # 4096^3 (256 tiles of 256) and larger keep the whole-tile plan and its
-    # tail split; the six workloads keep theirs (test_plans_for_the_workloads)
+    # one wave of 256 tiles of 256 (4096^3); 289 tiles: the bottom two tile
+    # rows split 4 ways (134 us against 156 on the 128 tile and 170 for
+    # whole tiles), unless K is short (4352^2 x 1024: the 128 tile, 45.4
+    # against 52.6 us); the six workloads keep their plans
+    # (test_plans_for_the_workloads)
     assert _plan((1, 4096, 4096, 4096)) == (256, 1)
-    assert describe(1, 4352, 4352, 4096)["tail_rows"] == "2"
+    p = describe(1, 4352, 4352, 4096)
+    assert (p["tile"][:3], p["tail_rows"], p["tail_split"]) == \
+        ("256", "2", "4")
+    assert _plan((1, 4352, 4352, 1024)) == (128, 1)
     # outside the model: K below 1024, operands stored along M, an element
     # loader (K % 8 != 0); and any forced tile or split
     assert _plan((1, 3072, 3072, 512)) == (128, 1)

@@ -154,3 +154,13 @@ def test_summarize_plan_grid_compares_the_planner_with_the_fastest(tmp_path):
         in lines
     assert lines[-1] == ("planner / fastest: mean 1.125, max 1.250 over 2 "
                          "shapes")
+    # a plan with a tail split is not among the grid's whole-tile choices:
+    # the planner's own run counts
+    p.write_text(json.dumps({
+        "shape": [1, 4352, 4352, 4096], "rounds": 4, "burst": 10,
+        "planner": {"tile": 256, "split": 1, "tail_rows": 2, "tail_split": 4,
+                    "us": 134.0},
+        "choices": [[256, 1, 170.0], [128, 1, 155.0]]}) + "\n")
+    lines = bench.summarize_plan_grid(str(p)).splitlines()
+    assert "| 1x4352x4352x4096 | 256 / 1 + tail 2 x 4 | 134.00 | 128 / 1 | " \
+        "155.00 | 0.865 |" in lines

@@ -32,10 +32,10 @@ def _run(g, fn, w, D):
 
 # (M, N, K, plan the planner must choose): the skinny workload (4 slices,
 # 8 MiB of partials), a smaller split (8 slices, 4 MiB), a tail split
-# (the bottom tile row in 3 slices, 12.6 MB), and splits of the cost model
+# (the bottom tile row in 4 slices, 16.8 MB), and splits of the cost model
 # (3 slices of 1536^2, 27 MiB; 16 slices of 1024^2, the whole 64 MiB)
 CASES = [(128, 4096, 8192, "split=4"), (64, 2048, 4096, "split=8"),
-         (4352, 4096, 1024, "tail_split=3"), (1536, 1536, 8192, "split=3"),
+         (4352, 4096, 2048, "tail_split=4"), (1536, 1536, 8192, "split=3"),
          (1024, 1024, 32768, "split=16")]
 
 

@@ -117,7 +117,7 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // at worst, 512^2 x 2048) and as fast as the fastest over 20 other shapes
 // up to 3072^2 x 8192; the rules used before were 17 % and 25 % slower on
 // average (71 % and 111 % at worst).
-constexpr int64_t kModelMinK = 1024;
+constexpr int64_t kModelMinK = 512;     // eight k-tiles
 constexpr int64_t kModelMinSliceK = 512;   // eight k-tiles per slice at least
 // Split factors tried: every one to 16, then about four per octave to 512.
 constexpr int kModelSplits[] = {1,  2,  3,  4,   5,   6,   7,   8,   9,
@@ -488,7 +488,7 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         while (!has_kernel(tile) && tile + 1 < NUM_TILES)
             ++tile;
     }
-    // K of 1024 or more on TN operands: tile and split-K factor from the
+    // K of 512 or more on TN operands: tile and split-K factor from the
     // cost model (a forced tile, split or tail split keeps the rules above
     // and below).
     int64_t model_splits = 0;

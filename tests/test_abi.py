@@ -244,7 +244,7 @@ def test_tail_split_plans(monkeypatch):
                   (64, 1024, 1024, 64), (1, 128, 4096, 8192)]:
         assert describe(*shape)["tail_rows"] == "0", shape
     # tiles with two workgroups per CU take no tail split by themselves
-    p = describe(1, 3072, 3072, 512)
+    p = describe(1, 3072, 3072, 448)
     assert p["tile"].startswith("128x128x") and p["tail_rows"] == "0"
     # too short a K for two slices of four k-tiles: no tail split
     assert describe(1, 4352, 4352, 448)["tail_rows"] == "0"
@@ -263,7 +263,7 @@ def _plan(shape, out="f16"):
 
 
 def test_cost_model_plans(monkeypatch):
-    """K of 1024 or more on TN operands: the tile and split-K factor (and,
+    """K of 512 or more on TN operands: the tile and split-K factor (and,
     on the 256 tile, the tail split) of least estimated time.  Each pin is
     the fastest of the choices timed on that shape."""
     # 144 or 225 tiles of 256: one partial wave of whole tiles, not the
@@ -298,9 +298,13 @@ def test_cost_model_plans(monkeypatch):
     assert (p["tile"][:3], p["tail_rows"], p["tail_split"]) == \
         ("256", "2", "4")
     assert _plan((1, 4352, 4352, 1024)) == (128, 1)
-    # outside the model: K below 1024, operands stored along M, an element
+    # K of 512 to 1023 (the fastest timed choice on each)
+    assert _plan((1, 1536, 1536, 768)) == (128, 1)
+    assert _plan((1, 3000, 3000, 960)) == (256, 1)
+    assert _plan((1, 1000, 1030, 1000), "f32") == (64, 1)
+    # outside the model: K below 512, operands stored along M, an element
     # loader (K % 8 != 0); and any forced tile or split
-    assert _plan((1, 3072, 3072, 512)) == (128, 1)
+    assert _plan((1, 3072, 3072, 448)) == (128, 1)
     assert describe(1, 3072, 3072, 4096, layouts=(1, 0))["tile"] \
         .startswith("128x128x")
     assert describe(1, 1500, 1700, 4100)["loader"] == "elem"

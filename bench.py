@@ -333,7 +333,8 @@ def plan_grid(shapes, rounds=4, burst=10):
     call of every tile x split-K choice (forced, slices of at least 256
     along K, partials within the no-allocation scratch) and of the
     planner's own choice, in interleaved bursts of `burst` calls, HIP
-    events around each burst.  One JSON line per shape."""
+    events around each burst.  One JSON line per shape.  A suffix "@la.lb"
+    stores A (la = 1) or B (lb = 1) along M or N instead of along K."""
     import statistics
     import torch
     import dense_gemm_fp16_amd as g
@@ -342,13 +343,16 @@ def plan_grid(shapes, rounds=4, burst=10):
         return -(-x // y)
 
     def plan_of(b, M, N, K, tail=False):
-        d = dict(kv.split("=") for kv in g.describe(b, M, N, K).split())
+        d = dict(kv.split("=") for kv in
+                 g.describe(b, M, N, K, layouts=lay).split())
         p = (int(d["tile"].split("x")[0]), int(d["split"]))
         return p + (int(d["tail_rows"]), int(d["tail_split"])) if tail else p
 
     gen = torch.Generator(device="cuda")
     for tok in shapes.split(","):
-        b, M, N, K = (int(x) for x in tok.split("x"))
+        dims, _, lays = tok.partition("@")
+        b, M, N, K = (int(x) for x in dims.split("x"))
+        lay = tuple(int(x) for x in lays.split(".")) if lays else (0, 0)
         specs = {}
         for tile in (256, 128, 64):
             if tile == 256 and (M < 256 or N < 256):
@@ -362,8 +366,14 @@ def plan_grid(shapes, rounds=4, burst=10):
                     break
                 specs.setdefault((tile, se), f"tile={tile},split={se},tail=0")
         gen.manual_seed(b * 7919 + M * 31 + N * 17 + K)
-        A = (torch.rand(b, M, K, device="cuda", generator=gen) * 2 - 1).half()
-        B = (torch.rand(b, N, K, device="cuda", generator=gen) * 2 - 1).half()
+        def operand(rows, along_rows):
+            if along_rows:     # stored K x rows, passed as a transposed view
+                x = torch.rand(b, K, rows, device="cuda", generator=gen)
+                return (x * 2 - 1).half().transpose(1, 2)
+            x = torch.rand(b, rows, K, device="cuda", generator=gen)
+            return (x * 2 - 1).half()
+        A = operand(M, lay[0] == 1)
+        B = operand(N, lay[1] == 1)
         D = torch.empty(b, M, N, device="cuda", dtype=torch.float16)
         runs = [("planner", "")] + [(k, v) for k, v in specs.items()]
         times = {k: [] for k, _ in runs}
@@ -394,7 +404,8 @@ def plan_grid(shapes, rounds=4, burst=10):
                 os.environ["GEMM_TN_FORCE"] = old
         med = {k: statistics.median(v) for k, v in times.items()}
         print(json.dumps({
-            "shape": [b, M, N, K], "rounds": rounds, "burst": burst,
+            "shape": [b, M, N, K], "layouts": list(lay), "rounds": rounds,
+            "burst": burst,
             "planner": {"tile": chosen[0], "split": chosen[1],
                         "tail_rows": chosen[2], "tail_split": chosen[3],
                         "us": round(med["planner"], 2)},
@@ -422,16 +433,21 @@ def summarize_plan_grid(path):
         t = own[0][2] if own else p["us"]
         ratios.append(t / best[2])
         b, M, N, K = r["shape"]
+        lay = r.get("layouts", [0, 0])
+        shape = f"{b}x{M}x{N}x{K}" + ("" if lay == [0, 0] else
+                                      f" @{lay[0]}.{lay[1]}")
         name = f"{p['tile']} / {p['split']}" + (
             f" + tail {tail} x {p['tail_split']}" if tail else "")
-        rows.append(f"| {b}x{M}x{N}x{K} | {name} | "
+        rows.append(f"| {shape} | {name} | "
                     f"{t:.2f} | {best[0]} / {best[1]} | {best[2]:.2f} | "
                     f"{t / best[2]:.3f} |")
     out = ["| batch x M x N x K | planner: tile / split | us | fastest: "
            "tile / split | us | ratio |", "|---|---|---|---|---|---|"]
     out += rows
-    out.append(f"\nplanner / fastest: mean {sum(ratios) / len(ratios):.3f}, "
-               f"max {max(ratios):.3f} over {len(ratios)} shapes")
+    if ratios:
+        out.append(f"\nplanner / fastest: mean "
+                   f"{sum(ratios) / len(ratios):.3f}, max {max(ratios):.3f} "
+                   f"over {len(ratios)} shapes")
     return "\n".join(out)
 
 

@@ -93,9 +93,10 @@ constexpr int64_t kOneKMinTiles = 512;  // fewer tiles: one per workgroup
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Cost model for problems with K of at least kModelMinK on TN operands with
-// 16-byte loads: the estimated time, in microseconds, of a tile and split-K
-// choice (on the 256 tile unsplit, with its tail split, tail_split_of).
+// Cost model for problems with K of at least kModelMinK and 16-byte loads:
+// the estimated time, in microseconds, of a tile and split-K choice (on the
+// 256 tile unsplit, with its tail split, tail_split_of).  Fitted on TN
+// operands; the other layouts' kernels rank the choices alike.
 //   - A workgroup costs kKtileUs[tile] per k-tile of its slice plus
 //     kFixedUs[tile] (its first loads and its epilogue); the 64 tile's
 //     split-K slices run on another kernel (four stages of 64-deep
@@ -265,18 +266,23 @@ inline double estimate_us(int tile, int64_t batch, int64_t M, int64_t N,
                        : 0.0);
 }
 
-// Tile and split-K factor of least estimated time.  The 256 tile is tried
-// when M and N are at least 256; splits while the slices keep
-// kModelMinSliceK and the partials fit in kModelMaxPartialBytes; a factor
-// that rounds to the slices of a smaller one is skipped.
-inline void choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
-                           int force_tail_rows, int *tile, int64_t *splits)
+// Tile and split-K factor of least estimated time, among the tiles set in
+// tile_mask (bit t: tile t has a kernel for the operands' layout).  The
+// 256 tile is tried when M and N are at least 256; splits while the slices
+// keep kModelMinSliceK and the partials fit in kModelMaxPartialBytes; a
+// factor that rounds to the slices of a smaller one is skipped.  Returns
+// false (and leaves tile and splits) when no tile is allowed.
+inline bool choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
+                           int force_tail_rows, unsigned tile_mask,
+                           int *tile, int64_t *splits)
 {
-    const int first = M >= 256 && N >= 256 ? TILE_256 : TILE_128;
-    double best = estimate_us(first, batch, M, N, K, 1, force_tail_rows);
-    *tile = first;
-    *splits = 1;
-    for (int t = first; t < NUM_TILES; ++t)
+    if (M < 256 || N < 256)
+        tile_mask &= ~(1u << TILE_256);
+    double best = 0.0;
+    bool found = false;
+    for (int t = 0; t < NUM_TILES; ++t) {
+        if (!((tile_mask >> t) & 1u))
+            continue;
         for (const int s : kModelSplits) {
             if (s > 1 && s * kModelMinSliceK > K)
                 break;
@@ -286,12 +292,15 @@ inline void choose_by_cost(int64_t batch, int64_t M, int64_t N, int64_t K,
                 break;
             const double us =
                 estimate_us(t, batch, M, N, K, s, force_tail_rows);
-            if (us < best) {
+            if (!found || us < best) {
                 best = us;
+                found = true;
                 *tile = t;
                 *splits = s;
             }
         }
+    }
+    return found;
 }
 
 inline bool mul_ok(int64_t a, int64_t b, int64_t *out)
@@ -488,13 +497,22 @@ inline Plan make_plan(int64_t batch, int64_t M, int64_t N, int64_t K,
         while (!has_kernel(tile) && tile + 1 < NUM_TILES)
             ++tile;
     }
-    // K of 512 or more on TN operands: tile and split-K factor from the
-    // cost model (a forced tile, split or tail split keeps the rules above
-    // and below).
+    // K of 512 or more with 16-byte loads, any layout: tile and split-K
+    // factor from the cost model (a forced tile, split or tail split keeps
+    // the rules above and below).
     int64_t model_splits = 0;
     if (o.tile < 0 && o.split < 1 && o.tail < 1 &&
-        loader == PLAN_LOAD_DIRECT && layout == 0 && K >= kModelMinK)
-        choose_by_cost(batch, M, N, K, o.tail, &tile, &model_splits);
+        loader == PLAN_LOAD_DIRECT && K >= kModelMinK) {
+        unsigned mask = 0;
+        for (int t = 0; t < NUM_TILES; ++t)
+            mask |= has_kernel(t) ? 1u << t : 0u;
+        int mt = tile;
+        int64_t ms = 0;
+        if (choose_by_cost(batch, M, N, K, o.tail, mask, &mt, &ms)) {
+            tile = mt;
+            model_splits = ms;
+        }
+    }
     // K within one k-tile, many tiles, 16-byte loads and stores: the
     // persistent one-k-tile kernel (128 x 128 tiles), which keeps the next
     // tile's operands in flight while a tile's results are written.

@@ -263,7 +263,7 @@ def _plan(shape, out="f16"):
 
 
 def test_cost_model_plans(monkeypatch):
-    """K of 512 or more on TN operands: the tile and split-K factor (and,
+    """K of 512 or more with 16-byte loads: the tile and split-K factor (and,
     on the 256 tile, the tail split) of least estimated time.  Each pin is
     the fastest of the choices timed on that shape."""
     # 144 or 225 tiles of 256: one partial wave of whole tiles, not the
@@ -302,11 +302,17 @@ def test_cost_model_plans(monkeypatch):
     assert _plan((1, 1536, 1536, 768)) == (128, 1)
     assert _plan((1, 3000, 3000, 960)) == (256, 1)
     assert _plan((1, 1000, 1030, 1000), "f32") == (64, 1)
-    # outside the model: K below 512, operands stored along M, an element
-    # loader (K % 8 != 0); and any forced tile or split
+    # operands stored along M or N: the same ranking (the 256 tile on eight
+    # waves at 3072^2 x 4096: 90.8 us against 108.1 on the 128 tile; 128
+    # tile in 3 slices at 1536^2 x 8192: 54.1 against 101.6 on the 64 tile)
+    p = describe(1, 3072, 3072, 4096, layouts=(1, 0))
+    assert (p["tile"][:3], p["split"], p["sched"]) == \
+        ("256", "1", "pingpong-split")
+    p = describe(1, 1536, 1536, 8192, layouts=(1, 1))
+    assert (p["tile"][:3], p["split"]) == ("128", "3")
+    # outside the model: K below 512, an element loader (K % 8 != 0); and
+    # any forced tile or split
     assert _plan((1, 3072, 3072, 448)) == (128, 1)
-    assert describe(1, 3072, 3072, 4096, layouts=(1, 0))["tile"] \
-        .startswith("128x128x")
     assert describe(1, 1500, 1700, 4100)["loader"] == "elem"
     monkeypatch.setenv("GEMM_TN_FORCE", "tile=128")
     assert _plan((1, 3072, 3072, 4096)) == (128, 1)
@@ -318,11 +324,12 @@ def test_split_rule_fills_one_wave():
     """Outside the cost model a split fills one wave of the tile: as many
     slices as the CUs hold workgroups of it (one per CU for the 256 tile,
     two for the others), never more."""
-    # 196 tiles of 256 (operands along M, so no cost model; K = 4096):
-    # one wave holds them whole, no split (on TN operands three slices, as
-    # the rule once chose, took 142 us against 80)
-    p = describe(1, 3584, 3584, 4096, layouts=(1, 0))
+    # 196 tiles of 256 (K % 8 != 0: element loads, no cost model): one wave
+    # holds them whole, no split (on TN operands three slices, as the rule
+    # once chose, took 142 us against 80)
+    p = describe(1, 3584, 3584, 4100)
     assert p["tile"].startswith("256x256x") and p["split"] == "1"
+    assert p["loader"] == "elem"
     # 165 tiles of 64 (element loader): 3 slices = 495 workgroups <= 512
     p = describe(1, 700, 900, 4100)
     assert p["tile"].startswith("64x64x") and p["split"] == "3"

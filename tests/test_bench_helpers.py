@@ -164,3 +164,16 @@ def test_summarize_plan_grid_compares_the_planner_with_the_fastest(tmp_path):
     lines = bench.summarize_plan_grid(str(p)).splitlines()
     assert "| 1x4352x4352x4096 | 256 / 1 + tail 2 x 4 | 134.00 | 128 / 1 | " \
         "155.00 | 0.865 |" in lines
+
+
+def test_summarize_plan_grid_names_the_layouts(tmp_path):
+    import json
+    p = tmp_path / "grid.jsonl"
+    p.write_text(json.dumps({
+        "shape": [1, 512, 512, 1024], "layouts": [1, 0], "rounds": 4,
+        "burst": 10, "planner": {"tile": 64, "split": 1, "tail_rows": 0,
+                                 "tail_split": 1, "us": 6.0},
+        "choices": [[64, 1, 6.0], [128, 1, 7.5]]}) + "\n")
+    lines = bench.summarize_plan_grid(str(p)).splitlines()
+    assert "| 1x512x512x1024 @1.0 | 64 / 1 | 6.00 | 64 / 1 | 6.00 | 1.000 |" \
+        in lines

@@ -75,10 +75,27 @@
 #ifndef GTN_W4_LOAD_EVERY
 #define GTN_W4_LOAD_EVERY 4
 #endif
-// Cache-policy bits of the staged 16-byte output stores (gfx950: 1 = sc0,
-// 2 = nt, 16 = sc1).
+// Most rows a wave stages through LDS per epilogue pass: with several
+// passes the stores of one pass leave while the next is staged.
+#ifndef GTN_EPI_MAX_RPP
+#define GTN_EPI_MAX_RPP 32
+#endif
+// Cache-policy bits of the staged 16-byte output stores of the one-k-tile
+// and attention kernels (gfx950: 1 = sc0, 2 = nt, 16 = sc1).
 #ifndef GTN_STORE_CPOL
 #define GTN_STORE_CPOL 2
+#endif
+// Cache-policy bits of the tile kernels' staged output (and split-K
+// partial) stores: sc1.  Measured against streaming (nt) stores with one
+// staging pass (HIP events, both builds interleaved in one process, same
+// box; bit-identical results), 32-row passes with sc1 stores took 4096^3
+// from 97.2-98.0 to 96.6-97.2 us, 4096 x 4096 x 1024 29.95 -> 29.13,
+// 128 x 4096 x 8192 (split) 20.5 -> 19.9, 1024^3 (fp32, C) 6.52 -> 6.29,
+// 1000 x 1030 x 1000 9.29 -> 8.89, 2048^3 24.0 -> 23.5; default-policy
+// stores were slower than either.  The one-k-tile kernel keeps nt stores
+// (sc1: 48.2 against 44.7-46.0 us on the score product).
+#ifndef GTN_TILE_STORE_CPOL
+#define GTN_TILE_STORE_CPOL 16
 #endif
 // Operand storages each tile has kernels for (bit L = layout L: bit 0 set
 // = A stored along M, bit 1 = B stored along N).  Direct loader: the

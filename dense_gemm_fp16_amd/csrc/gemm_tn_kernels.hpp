@@ -1164,7 +1164,10 @@ gemm_tn_kernel(GemmArgs p)
     constexpr int ROW_BYTES = WTN * ES;
     constexpr int CPR = ROW_BYTES / 16;               // 16-byte chunks per row
     constexpr int FIT = REGION / ROW_BYTES / 32 * 32;
-    constexpr int RPP = FIT < WTM ? FIT : WTM;        // rows per pass
+    // rows per pass: as many as the slice holds, at most GTN_EPI_MAX_RPP
+    constexpr int RPP_FIT = FIT < WTM ? FIT : WTM;
+    constexpr int RPP =
+        RPP_FIT < GTN_EPI_MAX_RPP ? RPP_FIT : GTN_EPI_MAX_RPP;
     constexpr int PASSES = WTM / RPP;
     static_assert(RPP >= 32 && WTM % RPP == 0, "LDS slice holds 32-row bands");
     static_assert(RPP * CPR % 64 == 0, "whole waves of 16-byte chunks");
@@ -1229,7 +1232,7 @@ gemm_tn_kernel(GemmArgs p)
                 region + roff[it % RPER] +
                 (it / RPER) * (RPER * (64 / CPR) * ROW_BYTES));
             __builtin_amdgcn_raw_buffer_store_b128(
-                v, rOut, base + (uint32_t)it * step, 0, GTN_STORE_CPOL);
+                v, rOut, base + (uint32_t)it * step, 0, GTN_TILE_STORE_CPOL);
         }
     };
 
@@ -1322,10 +1325,10 @@ gemm_tn_kernel(GemmArgs p)
                     n < N ? (uint32_t)((lm * ldd + n) * ES) : kOutOfRange;
                 if constexpr (ES == 4)
                     __builtin_amdgcn_raw_buffer_store_b32(
-                        *(const uint32_t *)src, rD, off, 0, GTN_STORE_CPOL);
+                        *(const uint32_t *)src, rD, off, 0, GTN_TILE_STORE_CPOL);
                 else
                     __builtin_amdgcn_raw_buffer_store_b16(
-                        *(const uint16_t *)src, rD, off, 0, GTN_STORE_CPOL);
+                        *(const uint16_t *)src, rD, off, 0, GTN_TILE_STORE_CPOL);
             }
         }
         return;

@@ -205,6 +205,15 @@ def _args():
                     help="also time torch.matmul (the vendor BLAS) on the "
                          "same inputs, interleaved with this library "
                          "(context only; plain products)")
+    ap.add_argument("--ab", metavar="LIB[@FORCE],...",
+                    help="time builds of the library against each other in "
+                         "one process: gemm_tn_ex of each shared library "
+                         "(optionally with a GEMM_TN_FORCE value, ';' for "
+                         "','), interleaved bursts over --ab-shapes")
+    ap.add_argument("--ab-shapes", default="1x4096x4096x4096",
+                    help="BxMxNxK[xOUT[xC]] list: OUT 1 = fp32 D, C 1 = "
+                         "alpha 1.5, beta 0.5 with a C read")
+    ap.add_argument("--ab-rounds", type=int, default=16)
     ap.add_argument("--plan-grid", nargs="?", const=PLAN_GRID_SHAPES,
                     metavar="BxMxNxK,...",
                     help="time every tile x split-K choice and the "
@@ -412,6 +421,94 @@ def plan_grid(shapes, rounds=4, burst=10):
             "choices": [[k[0], k[1], round(med[k], 2)] for k in specs]}),
             flush=True)
         del A, B, D
+
+
+def ab_compare(variants, shapes, rounds=16, burst=20):
+    """Builds of the library timed against each other in one process, so
+    that the machine's clock state is shared: each variant is a shared
+    library (built with `python -m dense_gemm_fp16_amd.build --defines ...
+    --out LIB`) whose gemm_tn_ex is called through ctypes, optionally with
+    a GEMM_TN_FORCE value after '@'.  Per shape, `rounds` rounds of a burst
+    of `burst` calls per variant (order reversed every other round), HIP
+    events around each burst; one JSON line with the median and minimum
+    time per call and whether every variant wrote the same bits."""
+    import ctypes
+    import statistics
+    import torch
+    i64, f32, vp, ci = (ctypes.c_int64, ctypes.c_float, ctypes.c_void_p,
+                        ctypes.c_int)
+    libs, vs = {}, []
+    for v in variants.split(","):
+        path, _, force = v.partition("@")
+        if path not in libs:
+            lib = ctypes.CDLL(os.path.abspath(path))
+            lib.gemm_tn_ex.argtypes = [i64, i64, i64, i64, f32, vp, ci, i64,
+                                       i64, vp, ci, i64, i64, f32, vp, i64,
+                                       i64, vp, i64, i64, ci, vp]
+            lib.gemm_tn_ex.restype = ci
+            libs[path] = lib
+        vs.append((v, libs[path], force.replace(";", ",")))
+    old = os.environ.get("GEMM_TN_FORCE")
+    try:
+        for tok in shapes.split(","):
+            dims = [int(x) for x in tok.split("x")]
+            b, M, N, K = dims[:4]
+            f32_out = len(dims) > 4 and dims[4] == 1
+            with_c = len(dims) > 5 and dims[5] == 1
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(b * 7919 + M * 31 + N * 17 + K)
+            A = (torch.rand(b, M, K, device="cuda", generator=gen) * 2 - 1)
+            B = (torch.rand(b, N, K, device="cuda", generator=gen) * 2 - 1)
+            A, B = A.half(), B.half()
+            dt = torch.float32 if f32_out else torch.float16
+            C = ((torch.rand(b, M, N, device="cuda", generator=gen) * 2 - 1)
+                 .to(dt) if with_c else None)
+            Ds = [torch.empty(b, M, N, device="cuda", dtype=dt) for _ in vs]
+            stream = torch.cuda.current_stream().cuda_stream
+            alpha, beta = (1.5, 0.5) if with_c else (1.0, 0.0)
+
+            def call(i):
+                _, lib, force = vs[i]
+                os.environ["GEMM_TN_FORCE"] = force
+                st = lib.gemm_tn_ex(
+                    b, M, N, K, alpha, A.data_ptr(), 0, K, M * K,
+                    B.data_ptr(), 0, K, N * K, beta,
+                    C.data_ptr() if with_c else None, N, M * N,
+                    Ds[i].data_ptr(), N, M * N, 1 if f32_out else 0, stream)
+                if st != 0:
+                    raise SystemExit(f"{vs[i][0]} {tok}: status {st}")
+
+            times = [[] for _ in vs]
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            for i in range(len(vs)):
+                for _ in range(3):
+                    call(i)
+            torch.cuda.synchronize()
+            for r in range(rounds):
+                order = range(len(vs)) if r % 2 == 0 else \
+                    reversed(range(len(vs)))
+                for i in order:
+                    call(i)
+                    call(i)
+                    e0.record()
+                    for _ in range(burst):
+                        call(i)
+                    e1.record()
+                    e1.synchronize()
+                    times[i].append(e0.elapsed_time(e1) * 1e3 / burst)
+            print(json.dumps({
+                "shape": tok, "rounds": rounds, "burst": burst,
+                "bitwise_same": all(torch.equal(Ds[0], d) for d in Ds[1:]),
+                "median_us": {v[0]: round(statistics.median(t), 2)
+                              for v, t in zip(vs, times)},
+                "min_us": {v[0]: round(min(t), 2)
+                           for v, t in zip(vs, times)}}), flush=True)
+    finally:
+        if old is None:
+            os.environ.pop("GEMM_TN_FORCE", None)
+        else:
+            os.environ["GEMM_TN_FORCE"] = old
 
 
 def summarize_plan_grid(path):
@@ -1088,6 +1185,9 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    if a.ab:
+        ab_compare(a.ab, a.ab_shapes, a.ab_rounds)
+        return
     if a.plan_grid:
         plan_grid(a.plan_grid)
         return

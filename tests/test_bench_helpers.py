@@ -177,3 +177,14 @@ def test_summarize_plan_grid_names_the_layouts(tmp_path):
     lines = bench.summarize_plan_grid(str(p)).splitlines()
     assert "| 1x512x512x1024 @1.0 | 64 / 1 | 6.00 | 64 / 1 | 6.00 | 1.000 |" \
         in lines
+
+
+def test_ab_mode_is_offered():
+    """`--ab` (builds of the library timed against each other in one
+    process) is part of the command line, with its shape syntax."""
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"),
+                        "--help"], capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0
+    assert "--ab LIB[@FORCE]" in r.stdout and "--ab-shapes" in r.stdout
+    assert callable(bench.ab_compare)
